@@ -1,0 +1,219 @@
+"""Throughput of the owner-rank Muon step on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+
+A step is one call of ``dmuon_muon_step`` over every matrix of the workload
+(momentum, per-slice normalisation, k = 5 quintic Newton–Schulz iterations,
+decoupled decay + lr-scaled update), with all inputs already resident in HBM.
+Prints one JSON line.  ``value`` is matrices stepped per second; the line also
+carries the effective TFLOP/s (Σ k·(4m²n + 2m³) per step), its share of the bf16
+dense matrix-core peak, a roofline entry for the dominant kernel (timed with HIP
+events on the launch stream during the timed steps) and the fp64 CPU oracle
+timed on a bounded sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0     # MI355X dense bf16 matrix-core peak (published)
+PEAK_HBM_GBS = 8000.0         # MI355X HBM3E (published)
+DEFAULT_WORKLOAD = "layer_d2048"
+
+
+def matrices_of(wl, share=None):
+    """(rows, cols, batch) of every stepped slice group."""
+    ts = wl.tensors if share is None else [wl.tensors[i] for i in share]
+    return ts
+
+
+def ns_flops(ts, steps):
+    tot = 0
+    for t in ts:
+        b = t.shape[0] if len(t.shape) == 3 else 1
+        r, c = t.shape[-2:]
+        m, n = min(r, c), max(r, c)
+        tot += b * steps * (4 * m * m * n + 2 * m ** 3)
+    return tot
+
+
+def phase_flops(ts):
+    """Algorithmic flops of one launch of each contraction phase (all slices)."""
+    g = s = a = 0
+    for t in ts:
+        b = t.shape[0] if len(t.shape) == 3 else 1
+        r, c = t.shape[-2:]
+        m, n = min(r, c), max(r, c)
+        g += b * 2 * m * m * n
+        s += b * 2 * m ** 3
+        a += b * 2 * m * m * n
+    return {"gram": g, "square": s, "apply": a}
+
+
+def n_slices(ts):
+    return sum(t.shape[0] if len(t.shape) == 3 else 1 for t in ts)
+
+
+def select_share(wl_name):
+    """The stepped tensors of a workload (one owner slot's LPT share for the 32-layer model)."""
+    from matrix_optimizer_muon_amd import lpt_assign
+    from matrix_optimizer_muon_amd.workloads import workload
+    wl = workload(wl_name)
+    if wl_name != "llama_d4096":
+        return wl, None
+    rows = [t.shape[0] for t in wl.tensors]
+    cols = [t.shape[1] for t in wl.tensors]
+    res = lpt_assign(rows, cols, [1] * len(rows), [t.layer for t in wl.tensors], 8, owner_slot=0)
+    return wl, [int(i) for i in res["owner_order"]]
+
+
+def cpu_baseline(wl, ts, budget_s=20.0):
+    """fp64 oracle on a bounded sample of the workload, scaled to matrices/s."""
+    import oracle
+    from matrix_optimizer_muon_amd.workloads import HYPER, make_tensor
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([p.get("num_threads", 1) for p in threadpool_info()
+                       if p.get("user_api") == "blas"] or [1])
+    except Exception:  # pragma: no cover
+        threads = os.cpu_count() or 1
+    # sample: whole tensors in workload order until the flop budget estimate is used
+    est_rate = 2.0e11     # fp64 flop/s assumed for the sample size only
+    chosen, fl = [], 0
+    for t in ts:
+        f = ns_flops([t], HYPER["steps"])
+        if chosen and (fl + f) / est_rate > budget_s:
+            break
+        chosen.append(t)
+        fl += f
+    # time only the oracle calls, not the input generation
+    total = 0.0
+    for t in chosen:
+        td = make_tensor(wl, t)
+        t1 = time.perf_counter()
+        oracle.muon_step(td.grad, td.momentum, td.master, lr=HYPER["lr"], mu=HYPER["mu"],
+                         wd=HYPER["wd"], eps=HYPER["eps"], a=HYPER["a"], b=HYPER["b"],
+                         c=HYPER["c"], steps=HYPER["steps"])
+        total += time.perf_counter() - t1
+    slices = n_slices(chosen)
+    return {"value": slices / total, "unit": "matrices/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"{len(chosen)} of {len(ts)} tensors ({slices} matrices) of the workload, "
+                      f"one full step each in fp64 numpy, {total:.2f} s",
+            "seconds": total, "gflops_fp64": ns_flops(chosen, HYPER["steps"]) / total / 1e9}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
+    ap.add_argument("--precision", default="bf16", choices=["bf16", "f32"])
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-phase-timing", action="store_true")
+    args = ap.parse_args()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one GPU only: the owner-rank step has no cross-GPU work on its "
+              "hot path (each GPU steps its own LPT share); run with --gpus 1", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+    import matrix_optimizer_muon_amd as mm
+    from matrix_optimizer_muon_amd.workloads import HYPER, make_tensor
+
+    wl, share = select_share(args.workload)
+    ts = matrices_of(wl, share)
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    grads, moms, masters = [], [], []
+    for t in ts:
+        td = make_tensor(wl, t)
+        if td.grad_bits is not None:
+            g = torch.from_numpy(td.grad_bits.view(np.int16)).view(torch.bfloat16).to(dev)
+        else:
+            g = torch.from_numpy(td.grad).to(dev)
+        grads.append(g)
+        moms.append(torch.from_numpy(td.momentum).to(dev))
+        masters.append(torch.from_numpy(td.master).to(dev))
+        del td
+    need = mm.muon_step_workspace_size(grads, moms, masters, precision=args.precision)
+    ws = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream()
+
+    def step():
+        mm.muon_step(grads, moms, masters, precision=args.precision, workspace=ws, stream=stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    if not args.no_phase_timing:
+        mm.phase_timing(True)
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    ev0.record(stream)
+    for _ in range(args.steps):
+        step()
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    mm.phase_timing(False)
+    phases = mm.phase_timing_read()
+    ms_step = ev0.elapsed_time(ev1) / args.steps
+    slices = n_slices(ts)
+    flops = ns_flops(ts, HYPER["steps"])
+    tflops = flops / (ms_step * 1e-3) / 1e12
+
+    roof = None
+    pf = phase_flops(ts)
+    if not args.no_phase_timing:
+        dom = max(("gram", "square", "apply"), key=lambda p: phases[p][0])
+        ms_tot, cnt = phases[dom]
+        if cnt:
+            avg_ms = ms_tot / cnt
+            ach = pf[dom] / (avg_ms * 1e-3) / 1e12
+            roof = {"kernel": dom, "bound": "mfma", "achieved": round(ach, 2),
+                    "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                    "frac": round(ach / PEAK_BF16_TFLOPS, 4), "traffic": None,
+                    "avg_launch_ms": round(avg_ms, 4), "flops_per_launch": pf[dom]}
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(wl, ts)
+
+    props = torch.cuda.get_device_properties(dev)
+    shapes = {}
+    for t in ts:
+        shapes[str(tuple(t.shape))] = shapes.get(str(tuple(t.shape)), 0) + 1
+    line = {
+        "metric": "Muon NS step matrices/s (+ effective TFLOP/s and % bf16 dense MFMA peak), 1xMI355X",
+        "value": round(slices / (ms_step * 1e-3), 3),
+        "unit": "matrices/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": args.precision, "data": "synthetic",
+        "tflops_effective": round(tflops, 2),
+        "pct_bf16_peak": round(100 * tflops / PEAK_BF16_TFLOPS, 2),
+        "config": {"workload": args.workload, "matrices": slices, "shapes": shapes,
+                   "ns_steps": HYPER["steps"], "grad_dtype": ts[0].grad_dtype,
+                   "effective_gflop_per_step": round(flops / 1e9, 1)},
+        "roofline": roof,
+        "cpu_baseline": cpu,
+        "phases_ms_per_step": {k: round(v[0] / args.steps, 4) for k, v in phases.items() if v[1]},
+        "wall_s_timed": round(wall, 3),
+        "device": {"name": props.name, "cus": props.multi_processor_count},
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,192 @@
+/*
+ * dmuon_ns.h — C ABI of libdmuon_ns, the owner-rank Muon optimizer step on one
+ * AMD Instinct MI355X (gfx950).
+ *
+ * What the library computes (sources: the DMuon documentation pages and the
+ * MindSpore parameter-grouping design page; see each entry point):
+ *
+ *   for every owned gradient tensor G (2-D, or 3-D = a batch of matrices over
+ *   the last two dims), with momentum buffer B and fp32 master weight W:
+ *     B ← μ·B + G
+ *     for each 2-D slice: X₀ = B_slice / (‖B_slice‖_F + eps), oriented so that
+ *       the Gram matrix is on the short side (a slice with rows > cols is
+ *       treated as its transpose); then k times
+ *       X ← a·X + b·(X Xᵀ) X + c·(X Xᵀ)² X;  O = X (original orientation)
+ *     W ← (1 − lr·wd)·W − lr·O
+ *
+ *   DMuon "架构设计" (Architecture design) page, §1 (the Newton–Schulz
+ *   equation with coefficients α, β, γ = a, b, c) and §2 (the owner alone runs
+ *   Newton–Schulz + momentum + weight decay + parameter update, on its local
+ *   full-precision copy, with no communication); HSDP guide, section "底层发生了
+ *   什么" (what happens underneath), step 3; routing page, dtype paragraph
+ *   (master and optimizer arithmetic in fp32); parameter-grouping page §2.1 /
+ *   §4.1 (fewer than 2 dims is an error) and §2.2 / §6 (more than 2 dims: the
+ *   matrix is the last two dims).
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * - Pointers named "device" must be device memory of the current HIP device;
+ *   tensors are dense and row-major (C order), last dim contiguous.
+ * - `stream` is a hipStream_t passed as void* (NULL = the null stream).  Every
+ *   GPU entry point only ENQUEUES work on `stream` and returns; the caller keeps
+ *   every buffer alive until that work completes.
+ * - The caller owns and frees all memory, including the workspace.  The library
+ *   allocates no device memory and keeps no state between calls, except the
+ *   opt-in phase-timing events (dmuon_phase_timing).
+ * - Every argument is validated on the host, before anything is enqueued, so a
+ *   rejected call leaves all buffers untouched.  Validation makes no HIP call.
+ * - Return value: DMUON_OK or a negative DMUON_E_* code; dmuon_last_error()
+ *   then gives a message (thread-local, valid until the next call on the thread).
+ * - After DMUON_E_HIP (a HIP launch/copy failed after validation) the contents
+ *   of the momentum, master and output buffers are unspecified.
+ * - Non-finite inputs are not checked; they propagate.
+ * - Results are deterministic: identical inputs give bit-identical outputs
+ *   (fixed-order reductions, no floating-point atomics).
+ */
+#ifndef DMUON_NS_H
+#define DMUON_NS_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum {
+  DMUON_OK = 0,
+  DMUON_E_NULL = -1,      /* a required pointer is NULL */
+  DMUON_E_NDIM = -2,      /* tensor with fewer than 2 (or more than 3) dims */
+  DMUON_E_SHAPE = -3,     /* negative or too large dimension, bad count */
+  DMUON_E_DTYPE = -4,     /* unknown dtype or precision code */
+  DMUON_E_CFG = -5,       /* bad hyper-parameter (k out of range, eps < 0, non-finite) */
+  DMUON_E_WORKSPACE = -6, /* workspace NULL, too small or misaligned */
+  DMUON_E_ALIAS = -7,     /* forbidden overlap between buffers */
+  DMUON_E_HIP = -8        /* HIP runtime error after validation */
+};
+
+typedef enum { DMUON_F32 = 0, DMUON_BF16 = 1 } dmuon_dtype;
+
+/* Arithmetic of the Newton–Schulz contractions.
+ * BF16_MFMA: bf16 matrix-core operands, fp32 accumulation, fp32 iterate.
+ * F32:       fp32 matrix-core operands and accumulation (parity path).
+ * Momentum, normalisation, the iterate's axpy and the update are fp32 in both. */
+typedef enum { DMUON_PREC_BF16_MFMA = 0, DMUON_PREC_F32 = 1 } dmuon_prec;
+
+/* One owned parameter.  shape = (rows, cols) for ndim 2 or (batch, rows, cols)
+ * for ndim 3 (only shape[0..ndim-1] are read).  Every dim must be ≥ 0 and
+ * rows, cols ≤ 65536; a tensor with a zero dim is skipped (no-op).
+ *   grad      device, read-only, grad_dtype (bf16 or fp32), the averaged gradient
+ *   momentum  device fp32, updated in place (B ← μB + G)
+ *   master    device fp32, updated in place (W ← (1 − lr·wd)W − lr·O)
+ *   ns_out    device fp32 or NULL: if set, receives O (same shape) as well
+ * grad must not overlap momentum, master or ns_out; momentum, master and ns_out
+ * must not overlap each other or another tensor's buffers (DMUON_E_ALIAS). */
+typedef struct {
+  int32_t ndim;
+  int32_t grad_dtype;       /* dmuon_dtype */
+  int64_t shape[3];
+  const void* grad;
+  float* momentum;
+  float* master;
+  float* ns_out;
+} dmuon_tensor;
+
+/* Step hyper-parameters.  lr, momentum (μ), weight_decay (wd): the HSDP guide's
+ * example builds the optimizer with lr 0.02 and momentum 0.95.  eps ≥ 0 is added
+ * to the Frobenius norm.  (a, b, c) are the page's (α, β, γ).  0 ≤ ns_steps ≤ 64.
+ * prec is a dmuon_prec. */
+typedef struct {
+  float lr;
+  float momentum;
+  float weight_decay;
+  float eps;
+  float a, b, c;
+  int32_t ns_steps;
+  int32_t prec;
+} dmuon_step_cfg;
+
+/* Bytes of workspace dmuon_muon_step needs for these tensors and cfg (host only,
+ * no HIP call).  The workspace must be device memory, 256-byte aligned. */
+int dmuon_muon_step_workspace_size(const dmuon_tensor* tensors, int32_t n_tensors,
+                                   const dmuon_step_cfg* cfg, size_t* bytes);
+
+/* The owner-rank Muon step over n_tensors tensors (all slices of all tensors in
+ * one grouped launch per phase): momentum, per-slice normalisation, ns_steps
+ * Newton–Schulz iterations, decoupled decay + lr-scaled update.
+ * DMuon architecture page §2 and §3.3 (owner-gated step); HSDP guide, "what
+ * happens underneath", step 3.  n_tensors ≥ 0 (0 is a no-op); tensors may be
+ * NULL only when n_tensors is 0.  The workspace (≥ the size reported above) is
+ * scratch: its contents on entry are ignored and on exit are unspecified. */
+int dmuon_muon_step(const dmuon_tensor* tensors, int32_t n_tensors, const dmuon_step_cfg* cfg,
+                    void* workspace, size_t workspace_bytes, void* stream);
+
+/* Bytes of workspace dmuon_ns_batched needs (host only, no HIP call). */
+int dmuon_ns_batched_workspace_size(int64_t batch, int64_t rows, int64_t cols, int32_t prec,
+                                    int32_t steps, size_t* bytes);
+
+/* Newton–Schulz alone on `batch` matrices rows×cols (contiguous, row-major):
+ * out[i] = NS_k(x[i]) with the architecture page §1 equation.  With normalize=1
+ * the start is x/(‖x‖_F + eps) per matrix; with normalize=0 it is x itself (for
+ * fixed-point checks).  x: device, x_dtype (bf16 or fp32), read-only.  out:
+ * device fp32, must not overlap x.  batch, rows, cols ≥ 0 (zero: no-op). */
+int dmuon_ns_batched(const void* x, int32_t x_dtype, float* out, int64_t batch, int64_t rows,
+                     int64_t cols, float a, float b, float c, int32_t steps, float eps,
+                     int32_t normalize, int32_t prec, void* workspace, size_t workspace_bytes,
+                     void* stream);
+
+/* Global greedy LPT partition of n Muon units over n_slots owner slots (host only,
+ * synchronous, no HIP call).  DMuon architecture page §3.1 (partition, global LPT):
+ * one pass over all units, largest first; units of one transformer layer go to
+ * distinct slots; same-layer units below merge_below_elems elements (0 = off; the
+ * page's default threshold is 5M) are merged into one unit with one owner.
+ *   rows, cols, batch, layer_id   host arrays of n items (batch ≥ 1; layer_id < 0:
+ *                                 no layer constraint)
+ *   cost_kind                     0: cost = batch·rows·cols; 1: NS flops
+ *                                 batch·(4m²n + 2m³), m = min, n = max
+ * Order: stable sort by cost, largest first (ties keep input order; a merged unit
+ * sits at its first member).  Each unit goes to the least-loaded slot holding no
+ * unit of its layer (ties: lowest slot id), or to the least-loaded slot if all
+ * hold its layer.
+ * Outputs (host arrays, caller-allocated):
+ *   slot_of[n]            slot of every item
+ *   slot_load[n_slots]    summed cost per slot
+ *   owner_order[n]        the items of owner_slot, grouped by exact shape
+ *                         (batch, rows, cols), groups in order of first
+ *                         assignment, items in assignment order; *n_owned of them
+ *   group_offsets[n + 1]  start of each group in owner_order, then *n_owned;
+ *                         *n_groups groups
+ * owner_order, n_owned, group_offsets and n_groups may all be NULL together. */
+int dmuon_lpt_assign(int64_t n, const int64_t* rows, const int64_t* cols, const int64_t* batch,
+                     const int32_t* layer_id, int32_t n_slots, int64_t merge_below_elems,
+                     int32_t cost_kind, int32_t* slot_of, int64_t* slot_load, int32_t owner_slot,
+                     int64_t* owner_order, int64_t* n_owned, int64_t* group_offsets,
+                     int32_t* n_groups);
+
+/* Plain NT product C = A·Bᵀ on the matrix-core kernel the step uses (a test hook
+ * for the contraction core).  A: M×K (lda elements per row), B: N×K (ldb), both
+ * dtype (bf16 or fp32), device; C: M×N fp32 (ldc), device.  lda and ldb must be
+ * multiples of 64 and the K..ld columns must be zero (they are summed). */
+int dmuon_gemm_nt(const void* A, const void* B, float* C, int64_t M, int64_t N, int64_t K,
+                  int64_t lda, int64_t ldb, int64_t ldc, int32_t dtype, void* stream);
+
+/* Phase timing for profiling (off by default).  enable = 1: every later kernel
+ * launch of the library is bracketed by two hipEvents on its stream; enable = 0
+ * stops it.  dmuon_phase_timing_read waits for the recorded events, writes for
+ * each phase p < n the summed milliseconds ms[p] and the launch count count[p],
+ * then clears the record.  Phases: 0 momentum+norm, 1 start (scale + operand
+ * copies), 2 Gram, 3 square+poly, 4 apply, 5 update (k = 0 only), 6 gemm_nt. */
+int dmuon_phase_timing(int32_t enable);
+int dmuon_phase_timing_read(double* ms, int64_t* count, int32_t n);
+
+/* Message for the last non-OK return on this thread ("" if none). */
+const char* dmuon_last_error(void);
+
+/* ABI version (bumped on any signature change). */
+int32_t dmuon_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* DMUON_NS_H */

@@ -1,0 +1,139 @@
+"""matrix_optimizer_muon_amd — the owner-rank Muon optimizer step on MI355X.
+
+Python face of libdmuon_ns (C ABI in ``include/dmuon_ns.h``).  The functions
+below only marshal arguments: momentum, normalisation, Newton–Schulz and the
+update all run in the library's HIP kernels on the caller's current stream.
+
+    muon_step(grads, momenta, masters, lr=0.02, momentum=0.95, ...)
+    ns_batched(x, coeffs=(3.4445, -4.775, 2.0315), steps=5, ...)
+    lpt_assign(rows, cols, batch, layer_id, n_slots, ...)   # host only
+"""
+from __future__ import annotations
+
+import ctypes
+
+from . import _binding as _b
+from .workloads import HYPER  # noqa: F401
+
+__all__ = ["muon_step", "muon_step_workspace_size", "ns_batched", "lpt_assign", "gemm_nt",
+           "phase_timing", "phase_timing_read", "abi_version", "load_library", "HYPER"]
+
+QUINTIC = (HYPER["a"], HYPER["b"], HYPER["c"])
+
+
+def load_library():
+    """Load the HIP library (raises RuntimeError if it is not built)."""
+    return _b.lib()
+
+
+def abi_version() -> int:
+    return int(_b.lib().dmuon_abi_version())
+
+
+def _cfg(lr, momentum, weight_decay, eps, coeffs, steps, precision):
+    return _b.make_cfg(lr, momentum, weight_decay, eps, coeffs, steps, precision)
+
+
+def muon_step_workspace_size(grads, momenta, masters, *, steps=5, precision="bf16",
+                             ns_outs=None) -> int:
+    cfg = _cfg(0.0, 0.0, 0.0, 0.0, QUINTIC, steps, precision)
+    descs = _b.make_descs(grads, momenta, masters, ns_outs)
+    return _b.muon_step_workspace_size(cfg, descs)
+
+
+def muon_step(grads, momenta, masters, *, lr=HYPER["lr"], momentum=HYPER["mu"],
+              weight_decay=HYPER["wd"], eps=HYPER["eps"], coeffs=QUINTIC, steps=HYPER["steps"],
+              precision="bf16", ns_outs=None, workspace=None, stream=None) -> None:
+    """One owner-rank Muon step over all given tensors, enqueued on ``stream``.
+
+    grads: bf16/fp32 GPU tensors (2-D or 3-D); momenta, masters: fp32, updated in
+    place; ns_outs: optional fp32 tensors that receive the Newton–Schulz output.
+    workspace: optional uint8 GPU tensor of at least ``muon_step_workspace_size``
+    bytes (allocated here when omitted).
+    """
+    cfg = _cfg(lr, momentum, weight_decay, eps, coeffs, steps, precision)
+    arr, n = _b.make_descs(grads, momenta, masters, ns_outs)
+    if n == 0:
+        return
+    need = _b.muon_step_workspace_size(cfg, (arr, n))
+    if workspace is None:
+        workspace = _b.alloc_workspace(need, grads[0].device)
+    L = _b.lib()
+    _b.check(L.dmuon_muon_step(arr, n, ctypes.byref(cfg), ctypes.c_void_p(workspace.data_ptr()),
+                               workspace.numel() * workspace.element_size(),
+                               _b._stream_handle(stream)))
+
+
+def ns_batched(x, *, coeffs=QUINTIC, steps=HYPER["steps"], eps=HYPER["eps"], normalize=True,
+               precision="bf16", out=None, workspace=None, stream=None):
+    """Newton–Schulz alone on a 2-D matrix or a 3-D batch (per slice); returns fp32."""
+    import torch
+    _b._check_dev(x, "x")
+    if x.dim() not in (2, 3):
+        raise ValueError("x must be 2-D or 3-D")
+    batch = 1 if x.dim() == 2 else x.shape[0]
+    rows, cols = x.shape[-2], x.shape[-1]
+    if out is None:
+        out = torch.empty(x.shape, dtype=torch.float32, device=x.device)
+    _b._check_dev(out, "out", torch.float32)
+    if out.shape != x.shape:
+        raise ValueError("out must have x's shape")
+    if precision not in _b.PREC:
+        raise ValueError(f"precision must be one of {sorted(_b.PREC)}")
+    L = _b.lib()
+    need = ctypes.c_size_t(0)
+    _b.check(L.dmuon_ns_batched_workspace_size(batch, rows, cols, _b.PREC[precision], int(steps),
+                                               ctypes.byref(need)))
+    if workspace is None:
+        workspace = _b.alloc_workspace(need.value, x.device)
+    a, b, c = coeffs
+    _b.check(L.dmuon_ns_batched(ctypes.c_void_p(x.data_ptr()), _b._dtype_code(x),
+                                ctypes.c_void_p(out.data_ptr()), batch, rows, cols, a, b, c,
+                                int(steps), eps, 1 if normalize else 0, _b.PREC[precision],
+                                ctypes.c_void_p(workspace.data_ptr()),
+                                workspace.numel() * workspace.element_size(),
+                                _b._stream_handle(stream)))
+    return out
+
+
+def gemm_nt(A, B, K=None, stream=None):
+    """C = A·Bᵀ (fp32) on the step's matrix-core contraction kernel (test hook).
+
+    A: M×lda, B: N×ldb (bf16 or fp32, same dtype, ld multiples of 64); only the
+    first K columns are meant, the rest must be zero.
+    """
+    import torch
+    _b._check_dev(A, "A")
+    _b._check_dev(B, "B")
+    if A.dtype != B.dtype:
+        raise ValueError("A and B must share a dtype")
+    M, lda = A.shape
+    N, ldb = B.shape
+    K = lda if K is None else K
+    C = torch.empty((M, N), dtype=torch.float32, device=A.device)
+    _b.check(_b.lib().dmuon_gemm_nt(ctypes.c_void_p(A.data_ptr()), ctypes.c_void_p(B.data_ptr()),
+                                    ctypes.c_void_p(C.data_ptr()), M, N, K, lda, ldb, N,
+                                    _b._dtype_code(A), _b._stream_handle(stream)))
+    return C
+
+
+def lpt_assign(rows, cols, batch, layer_id, n_slots, *, merge_below_elems=0, cost_kind=0,
+               owner_slot=0):
+    """Global LPT partition (host only, synchronous); see ``dmuon_lpt_assign``."""
+    return _b.lpt_assign_np(rows, cols, batch, layer_id, n_slots, merge_below_elems, cost_kind,
+                            owner_slot)
+
+
+def phase_timing(enable: bool) -> None:
+    _b.check(_b.lib().dmuon_phase_timing(1 if enable else 0))
+
+
+def phase_timing_read():
+    """{phase: (ms_total, launches)} of the launches since the last read."""
+    import numpy as np
+    n = len(_b.PHASES)
+    ms = np.zeros(n, dtype=np.float64)
+    cnt = np.zeros(n, dtype=np.int64)
+    _b.check(_b.lib().dmuon_phase_timing_read(ms.ctypes.data_as(ctypes.c_void_p),
+                                              cnt.ctypes.data_as(ctypes.c_void_p), n))
+    return {name: (float(ms[i]), int(cnt[i])) for i, name in enumerate(_b.PHASES)}

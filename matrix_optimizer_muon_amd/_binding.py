@@ -1,0 +1,204 @@
+"""ctypes binding of libdmuon_ns (argument marshalling only).
+
+Every step of the Muon path runs in the HIP library; this module only turns
+torch tensors into pointers, sizes and a stream handle, and error codes into
+exceptions.  If the library is not built the calls raise: there is no fallback.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import numpy as np
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libdmuon_ns.so")
+
+DMUON_OK = 0
+ERRORS = {
+    -1: ("DMUON_E_NULL", ValueError),
+    -2: ("DMUON_E_NDIM", ValueError),
+    -3: ("DMUON_E_SHAPE", ValueError),
+    -4: ("DMUON_E_DTYPE", ValueError),
+    -5: ("DMUON_E_CFG", ValueError),
+    -6: ("DMUON_E_WORKSPACE", ValueError),
+    -7: ("DMUON_E_ALIAS", ValueError),
+    -8: ("DMUON_E_HIP", RuntimeError),
+}
+F32, BF16 = 0, 1
+PREC = {"bf16": 0, "f32": 1}
+PHASES = ["momentum", "start", "gram", "square", "apply", "update", "gemm_nt"]
+EXPORTED = ["dmuon_muon_step_workspace_size", "dmuon_muon_step", "dmuon_ns_batched_workspace_size",
+            "dmuon_ns_batched", "dmuon_lpt_assign", "dmuon_gemm_nt", "dmuon_phase_timing",
+            "dmuon_phase_timing_read", "dmuon_last_error", "dmuon_abi_version"]
+
+
+class DmuonError(Exception):
+    pass
+
+
+class Tensor(ctypes.Structure):
+    _fields_ = [("ndim", ctypes.c_int32), ("grad_dtype", ctypes.c_int32),
+                ("shape", ctypes.c_int64 * 3), ("grad", ctypes.c_void_p),
+                ("momentum", ctypes.c_void_p), ("master", ctypes.c_void_p),
+                ("ns_out", ctypes.c_void_p)]
+
+
+class StepCfg(ctypes.Structure):
+    _fields_ = [("lr", ctypes.c_float), ("momentum", ctypes.c_float),
+                ("weight_decay", ctypes.c_float), ("eps", ctypes.c_float),
+                ("a", ctypes.c_float), ("b", ctypes.c_float), ("c", ctypes.c_float),
+                ("ns_steps", ctypes.c_int32), ("prec", ctypes.c_int32)]
+
+
+_lib = None
+
+
+def lib():
+    """Load libdmuon_ns.so (built in-tree); raise if it is missing."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(f"{LIB_PATH} is not built: run `python -m matrix_optimizer_muon_amd.build`")
+    L = ctypes.CDLL(LIB_PATH)
+    vp, i32, i64, f32, sz = (ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_float,
+                             ctypes.c_size_t)
+    P = ctypes.POINTER
+    L.dmuon_muon_step_workspace_size.argtypes = [P(Tensor), i32, P(StepCfg), P(sz)]
+    L.dmuon_muon_step.argtypes = [P(Tensor), i32, P(StepCfg), vp, sz, vp]
+    L.dmuon_ns_batched_workspace_size.argtypes = [i64, i64, i64, i32, i32, P(sz)]
+    L.dmuon_ns_batched.argtypes = [vp, i32, vp, i64, i64, i64, f32, f32, f32, i32, f32, i32, i32,
+                                   vp, sz, vp]
+    L.dmuon_lpt_assign.argtypes = [i64, vp, vp, vp, vp, i32, i64, i32, vp, vp, i32, vp, vp, vp, vp]
+    L.dmuon_gemm_nt.argtypes = [vp, vp, vp, i64, i64, i64, i64, i64, i64, i32, vp]
+    L.dmuon_phase_timing.argtypes = [i32]
+    L.dmuon_phase_timing_read.argtypes = [vp, vp, i32]
+    L.dmuon_last_error.restype = ctypes.c_char_p
+    L.dmuon_last_error.argtypes = []
+    L.dmuon_abi_version.restype = i32
+    for name in ["dmuon_muon_step_workspace_size", "dmuon_muon_step",
+                 "dmuon_ns_batched_workspace_size", "dmuon_ns_batched", "dmuon_lpt_assign",
+                 "dmuon_gemm_nt", "dmuon_phase_timing", "dmuon_phase_timing_read"]:
+        getattr(L, name).restype = ctypes.c_int
+    _lib = L
+    return L
+
+
+def check(code: int) -> None:
+    if code == DMUON_OK:
+        return
+    name, exc = ERRORS.get(code, ("DMUON_E_?", RuntimeError))
+    msg = lib().dmuon_last_error().decode(errors="replace")
+    err = exc(f"{name}: {msg}")
+    err.code = code
+    raise err
+
+
+# --------------------------------------------------------------------------
+# torch-facing helpers
+# --------------------------------------------------------------------------
+def _torch():
+    import torch
+    return torch
+
+
+def _stream_handle(stream):
+    torch = _torch()
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _dtype_code(t):
+    torch = _torch()
+    if t.dtype == torch.bfloat16:
+        return BF16
+    if t.dtype == torch.float32:
+        return F32
+    raise ValueError(f"gradient dtype must be bfloat16 or float32, got {t.dtype}")
+
+
+def _check_dev(t, what, dtype=None):
+    torch = _torch()
+    if not isinstance(t, torch.Tensor):
+        raise ValueError(f"{what} must be a torch.Tensor")
+    if t.device.type != "cuda":
+        raise ValueError(f"{what} must be a GPU tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{what} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise ValueError(f"{what} must be {dtype}, got {t.dtype}")
+
+
+def make_cfg(lr, momentum, weight_decay, eps, coeffs, steps, precision) -> StepCfg:
+    if precision not in PREC:
+        raise ValueError(f"precision must be one of {sorted(PREC)}")
+    a, b, c = coeffs
+    return StepCfg(lr, momentum, weight_decay, eps, a, b, c, int(steps), PREC[precision])
+
+
+def make_descs(grads, momenta, masters, ns_outs=None):
+    torch = _torch()
+    n = len(grads)
+    if not (len(momenta) == len(masters) == n):
+        raise ValueError("grads, momenta and masters differ in length")
+    if ns_outs is not None and len(ns_outs) != n:
+        raise ValueError("ns_outs differs in length")
+    arr = (Tensor * max(n, 1))()
+    for i in range(n):
+        g, m, w = grads[i], momenta[i], masters[i]
+        o = None if ns_outs is None else ns_outs[i]
+        _check_dev(g, f"grads[{i}]")
+        _check_dev(m, f"momenta[{i}]", torch.float32)
+        _check_dev(w, f"masters[{i}]", torch.float32)
+        if o is not None:
+            _check_dev(o, f"ns_outs[{i}]", torch.float32)
+        if m.shape != g.shape or w.shape != g.shape or (o is not None and o.shape != g.shape):
+            raise ValueError(f"tensor {i}: shapes of grad, momentum, master (and ns_out) differ")
+        arr[i].ndim = g.dim()
+        for d in range(min(g.dim(), 3)):
+            arr[i].shape[d] = g.shape[d]
+        arr[i].grad_dtype = _dtype_code(g)
+        arr[i].grad = g.data_ptr()
+        arr[i].momentum = m.data_ptr()
+        arr[i].master = w.data_ptr()
+        arr[i].ns_out = None if o is None else o.data_ptr()
+    return arr, n
+
+
+def muon_step_workspace_size(cfg: StepCfg, descs) -> int:
+    arr, n = descs
+    out = ctypes.c_size_t(0)
+    check(lib().dmuon_muon_step_workspace_size(arr, n, ctypes.byref(cfg), ctypes.byref(out)))
+    return out.value
+
+
+def alloc_workspace(nbytes, device):
+    torch = _torch()
+    return torch.empty(max(int(nbytes), 1), dtype=torch.uint8, device=device)
+
+
+def lpt_assign_np(rows, cols, batch, layer_id, n_slots, merge_below_elems=0, cost_kind=0,
+                  owner_slot=0):
+    """Host-only LPT (no GPU needed); numpy in, dict of numpy out."""
+    rows = np.ascontiguousarray(rows, dtype=np.int64)
+    cols = np.ascontiguousarray(cols, dtype=np.int64)
+    batch = np.ascontiguousarray(batch, dtype=np.int64)
+    layer_id = np.ascontiguousarray(layer_id, dtype=np.int32)
+    n = rows.shape[0]
+    slot_of = np.empty(max(n, 1), dtype=np.int32)
+    slot_load = np.empty(max(n_slots, 1), dtype=np.int64)
+    owner_order = np.empty(max(n, 1), dtype=np.int64)
+    n_owned = ctypes.c_int64(0)
+    offsets = np.empty(n + 1, dtype=np.int64)
+    n_groups = ctypes.c_int32(0)
+    ptr = lambda a: a.ctypes.data_as(ctypes.c_void_p)  # noqa: E731
+    check(lib().dmuon_lpt_assign(n, ptr(rows), ptr(cols), ptr(batch), ptr(layer_id), n_slots,
+                                 merge_below_elems, cost_kind, ptr(slot_of), ptr(slot_load),
+                                 owner_slot, ptr(owner_order), ctypes.byref(n_owned),
+                                 ptr(offsets), ctypes.byref(n_groups)))
+    k = n_owned.value
+    g = n_groups.value
+    return {"slot_of": slot_of[:n].copy(), "slot_load": slot_load[:n_slots].copy(),
+            "owner_order": owner_order[:k].copy(), "group_offsets": offsets[:g + 1].copy()}

@@ -1,0 +1,469 @@
+// C entry points of libdmuon_ns: validation, planning, launch sequence, timing.
+//
+// The step follows the DMuon "架构设计" (Architecture design) page: §1 gives the
+// Newton–Schulz equation, §2 says only the owner runs NS + momentum + weight
+// decay + parameter update on its local full-precision copy without any
+// communication; the HSDP guide ("what happens underneath", step 3) repeats it.
+// Rank checks follow the MindSpore parameter-grouping page §2.1 / §4.1 (fewer
+// than two dims is an error) and §2.2 / §6 (the matrix is the last two dims).
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cmath>
+#include <cstdio>
+#include <cstdlib>
+#include <cstring>
+#include <mutex>
+#include <string>
+#include <vector>
+
+#include "../../include/dmuon_ns.h"
+#include "internal.hpp"
+
+namespace dmuon {
+
+static thread_local std::string g_err;
+
+static int fail(int code, const std::string& msg) {
+  g_err = msg;
+  return code;
+}
+
+int lpt_fail(int code, const char* msg) { return fail(code, msg); }
+void clear_error() { g_err.clear(); }
+
+// ---------------------------------------------------------------------------
+// phase timing (opt-in)
+// ---------------------------------------------------------------------------
+struct TimedLaunch {
+  int phase;
+  hipEvent_t a, b;
+};
+static std::mutex g_tmu;
+static bool g_timing = false;
+static std::vector<TimedLaunch> g_timed;
+static std::vector<hipEvent_t> g_evpool;
+static hipEvent_t g_pending = nullptr;
+
+static hipEvent_t take_event() {
+  if (!g_evpool.empty()) {
+    hipEvent_t e = g_evpool.back();
+    g_evpool.pop_back();
+    return e;
+  }
+  hipEvent_t e = nullptr;
+  if (hipEventCreate(&e) != hipSuccess) return nullptr;
+  return e;
+}
+
+void timing_before(int phase, void* stream) {
+  (void)phase;
+  std::lock_guard<std::mutex> lk(g_tmu);
+  if (!g_timing) return;
+  g_pending = take_event();
+  if (g_pending) (void)hipEventRecord(g_pending, (hipStream_t)stream);
+}
+
+void timing_after(int phase, void* stream) {
+  std::lock_guard<std::mutex> lk(g_tmu);
+  if (!g_timing || !g_pending) return;
+  hipEvent_t b = take_event();
+  if (!b) return;
+  (void)hipEventRecord(b, (hipStream_t)stream);
+  g_timed.push_back({phase, g_pending, b});
+  g_pending = nullptr;
+}
+
+// ---------------------------------------------------------------------------
+// planning
+// ---------------------------------------------------------------------------
+struct Item {
+  int64_t batch, rows, cols;
+  const void* grad;
+  int grad_bf16;
+  float* mom;
+  float* master;
+  float* out;
+};
+
+struct Plan {
+  std::vector<DevProblem> probs;
+  std::vector<int32_t> prefix;      // PH_COUNT × (n + 1)
+  int64_t total_slices = 0;
+  int64_t total_wg[PH_COUNT] = {};
+  size_t off_prefix = 0, off_scal = 0, table_bytes = 0, bytes = 0;
+};
+
+static size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+// Lay out the workspace for the items; with base == nullptr only sizes are computed.
+static int build_plan(const std::vector<Item>& items, int prec_f32, Plan& pl, char* base) {
+  const size_t esz = prec_f32 ? 4 : 2;
+  const int n = (int)items.size();
+  pl.probs.assign(n, DevProblem{});
+  pl.prefix.assign((size_t)PH_COUNT * (n + 1), 0);
+  size_t off = align256((size_t)n * sizeof(DevProblem));
+  pl.off_prefix = off;
+  off = align256(off + pl.prefix.size() * sizeof(int32_t));
+  pl.table_bytes = off;
+  int64_t slices = 0;
+  for (const Item& it : items) slices += it.batch;
+  pl.total_slices = slices;
+  pl.off_scal = off;
+  off = align256(off + (size_t)slices * kScalStride * sizeof(float));
+
+  int64_t wg[PH_COUNT] = {};
+  int64_t slice_base = 0;
+  auto carve = [&](size_t bytes) -> char* {
+    char* p = base ? base + off : nullptr;
+    off = align256(off + bytes);
+    return p;
+  };
+  for (int i = 0; i < n; ++i) {
+    const Item& it = items[i];
+    DevProblem& P = pl.probs[i];
+    P.batch = (int32_t)it.batch;
+    P.rows = (int32_t)it.rows;
+    P.cols = (int32_t)it.cols;
+    P.wide = it.rows <= it.cols ? 1 : 0;
+    P.m = (int32_t)std::min(it.rows, it.cols);
+    P.n = (int32_t)std::max(it.rows, it.cols);
+    P.ld_m = (int32_t)round_up(P.m, kLdAlign);
+    P.ld_n = (int32_t)round_up(P.n, kLdAlign);
+    P.grad_bf16 = it.grad_bf16;
+    const int64_t per = it.rows * it.cols;
+    P.chunks = (int32_t)cdiv(per, kElemChunk);
+    P.prep_tiles_r = (int32_t)cdiv(it.rows, kPrepTile);
+    P.prep_tiles_c = (int32_t)cdiv(it.cols, kPrepTile);
+    P.tiles_m = (int32_t)cdiv(P.m, kTile);
+    P.apply_tr = (int32_t)cdiv(it.rows, kTile);
+    P.apply_tc = (int32_t)cdiv(it.cols, kTile);
+    P.slice_base = (int32_t)slice_base;
+    slice_base += it.batch;
+    P.grad = it.grad;
+    P.mom = it.mom;
+    P.master = it.master;
+    P.out = it.out;
+    const int64_t b = it.batch;
+    P.xf = (float*)carve((size_t)(b * per) * 4);
+    P.xg = carve((size_t)(b * P.m * P.ld_n) * esz);
+    P.xa0 = carve((size_t)(b * P.n * P.ld_m) * esz);
+    P.xa1 = carve((size_t)(b * P.n * P.ld_m) * esz);
+    P.ap = carve((size_t)(b * P.m * P.ld_m) * esz);
+    P.bp = carve((size_t)(b * P.m * P.ld_m) * esz);
+    P.part_norm = (float*)carve((size_t)(b * P.chunks) * 4);
+    P.part_apply = (float*)carve((size_t)(b * P.apply_tr * P.apply_tc) * 4);
+    const int64_t tri = (int64_t)P.tiles_m * (P.tiles_m + 1) / 2;
+    const int64_t cnt[PH_COUNT] = {b * P.chunks, b * P.prep_tiles_r * P.prep_tiles_c, b * tri, b * tri,
+                                   b * P.apply_tr * P.apply_tc, b * P.chunks, 0};
+    for (int ph = 0; ph < PH_COUNT; ++ph) {
+      P.wg0[ph] = (int32_t)wg[ph];
+      pl.prefix[(size_t)ph * (n + 1) + i] = (int32_t)wg[ph];
+      wg[ph] += cnt[ph];
+      if (wg[ph] > INT32_MAX) return fail(DMUON_E_SHAPE, "too many workgroups in one launch");
+    }
+  }
+  for (int ph = 0; ph < PH_COUNT; ++ph) {
+    pl.prefix[(size_t)ph * (n + 1) + n] = (int32_t)wg[ph];
+    pl.total_wg[ph] = wg[ph];
+  }
+  pl.bytes = off;
+  return DMUON_OK;
+}
+
+static int run_plan(Plan& pl, char* ws, int prec_f32, const LaunchScalars& base_s, int steps, void* stream) {
+  // descriptors + prefix arrays: one host → device copy, ordered on the stream
+  std::vector<char> host(pl.table_bytes, 0);
+  std::memcpy(host.data(), pl.probs.data(), pl.probs.size() * sizeof(DevProblem));
+  std::memcpy(host.data() + pl.off_prefix, pl.prefix.data(), pl.prefix.size() * sizeof(int32_t));
+  int e = upload_async(ws, host.data(), host.size(), stream);
+  if (e) return fail(DMUON_E_HIP, std::string("table upload: ") + hip_error_string(e));
+  LaunchTable tab;
+  tab.probs = (const DevProblem*)ws;
+  tab.wg_prefix = (const int32_t*)(ws + pl.off_prefix);
+  tab.scal = (float*)(ws + pl.off_scal);
+  tab.n_probs = (int32_t)pl.probs.size();
+  auto go = [&](int ph, const LaunchScalars& s) -> int {
+    tab.total_wg = (int32_t)pl.total_wg[ph];
+    const int r = launch_phase(ph, prec_f32, tab, s, stream);
+    if (r) return fail(DMUON_E_HIP, std::string("launch failed: ") + hip_error_string(r));
+    return DMUON_OK;
+  };
+  LaunchScalars s = base_s;
+  s.t = 0;
+  s.last = 0;
+  if ((e = go(PH_MOMENTUM, s))) return e;
+  if ((e = go(PH_START, s))) return e;
+  if (steps == 0) return go(PH_UPDATE, s);
+  for (int t = 0; t < steps; ++t) {
+    s.t = t;
+    s.last = t == steps - 1;
+    if ((e = go(PH_GRAM, s))) return e;
+    if ((e = go(PH_SQUARE, s))) return e;
+    if ((e = go(PH_APPLY, s))) return e;
+  }
+  return DMUON_OK;
+}
+
+// ---------------------------------------------------------------------------
+// validation helpers
+// ---------------------------------------------------------------------------
+struct Range {
+  uintptr_t lo, hi;
+  bool ro;
+};
+
+static int check_alias(std::vector<Range>& rs) {
+  std::sort(rs.begin(), rs.end(), [](const Range& a, const Range& b) { return a.lo < b.lo; });
+  // sweep: any writable range must not intersect any other range
+  uintptr_t max_hi_any = 0, max_hi_w = 0;
+  for (size_t i = 0; i < rs.size(); ++i) {
+    const Range& r = rs[i];
+    if (i > 0) {
+      if (r.lo < max_hi_w) return fail(DMUON_E_ALIAS, "buffers overlap (a written buffer is shared)");
+      if (!r.ro && r.lo < max_hi_any) return fail(DMUON_E_ALIAS, "buffers overlap (a written buffer is shared)");
+    }
+    max_hi_any = std::max(max_hi_any, r.hi);
+    if (!r.ro) max_hi_w = std::max(max_hi_w, r.hi);
+  }
+  return DMUON_OK;
+}
+
+static bool finite(float x) { return std::isfinite(x); }
+
+static int check_cfg(const dmuon_step_cfg* cfg) {
+  if (!cfg) return fail(DMUON_E_NULL, "cfg is NULL");
+  if (cfg->prec != DMUON_PREC_BF16_MFMA && cfg->prec != DMUON_PREC_F32)
+    return fail(DMUON_E_DTYPE, "unknown precision code " + std::to_string(cfg->prec));
+  if (cfg->ns_steps < 0 || cfg->ns_steps > kMaxSteps)
+    return fail(DMUON_E_CFG, "ns_steps must be in [0, 64], got " + std::to_string(cfg->ns_steps));
+  if (!finite(cfg->eps) || cfg->eps < 0.f) return fail(DMUON_E_CFG, "eps must be finite and >= 0");
+  if (!finite(cfg->lr) || !finite(cfg->momentum) || !finite(cfg->weight_decay) || !finite(cfg->a) ||
+      !finite(cfg->b) || !finite(cfg->c))
+    return fail(DMUON_E_CFG, "hyper-parameters must be finite");
+  return DMUON_OK;
+}
+
+static int collect_items(const dmuon_tensor* t, int32_t n, std::vector<Item>& items, std::vector<Range>* rs) {
+  if (n < 0) return fail(DMUON_E_SHAPE, "n_tensors < 0");
+  if (n > 0 && !t) return fail(DMUON_E_NULL, "tensors is NULL");
+  for (int32_t i = 0; i < n; ++i) {
+    const dmuon_tensor& x = t[i];
+    const std::string who = "tensor " + std::to_string(i) + ": ";
+    if (x.ndim < 2) return fail(DMUON_E_NDIM, who + "Muon needs >= 2 dims (1-D parameters belong to an element-wise optimizer)");
+    if (x.ndim > 3) return fail(DMUON_E_NDIM, who + "at most 3 dims (batch, rows, cols) are supported");
+    for (int d = 0; d < x.ndim; ++d)
+      if (x.shape[d] < 0) return fail(DMUON_E_SHAPE, who + "negative dim");
+    if (x.grad_dtype != DMUON_F32 && x.grad_dtype != DMUON_BF16)
+      return fail(DMUON_E_DTYPE, who + "grad_dtype must be DMUON_F32 or DMUON_BF16");
+    const int64_t batch = x.ndim == 3 ? x.shape[0] : 1;
+    const int64_t rows = x.shape[x.ndim - 2], cols = x.shape[x.ndim - 1];
+    if (rows > 65536 || cols > 65536) return fail(DMUON_E_SHAPE, who + "rows and cols must be <= 65536");
+    if (batch > (int64_t)1 << 30) return fail(DMUON_E_SHAPE, who + "batch too large");
+    const int64_t numel = batch * rows * cols;
+    if (numel == 0) continue;
+    if (!x.grad || !x.momentum || !x.master) return fail(DMUON_E_NULL, who + "grad, momentum and master must be set");
+    if (rs) {
+      const size_t gs = x.grad_dtype == DMUON_BF16 ? 2 : 4;
+      rs->push_back({(uintptr_t)x.grad, (uintptr_t)x.grad + numel * gs, true});
+      rs->push_back({(uintptr_t)x.momentum, (uintptr_t)x.momentum + numel * 4, false});
+      rs->push_back({(uintptr_t)x.master, (uintptr_t)x.master + numel * 4, false});
+      if (x.ns_out) rs->push_back({(uintptr_t)x.ns_out, (uintptr_t)x.ns_out + numel * 4, false});
+    }
+    items.push_back({batch, rows, cols, x.grad, x.grad_dtype == DMUON_BF16, x.momentum, x.master, x.ns_out});
+  }
+  return DMUON_OK;
+}
+
+static int check_workspace(void* ws, size_t have, size_t need) {
+  if (need == 0) return DMUON_OK;
+  if (!ws) return fail(DMUON_E_WORKSPACE, "workspace is NULL");
+  if ((uintptr_t)ws & 255) return fail(DMUON_E_WORKSPACE, "workspace must be 256-byte aligned");
+  if (have < need)
+    return fail(DMUON_E_WORKSPACE, "workspace too small: need " + std::to_string(need) + " bytes, got " +
+                                       std::to_string(have));
+  return DMUON_OK;
+}
+
+static int test_fail_hook() {
+  // DMUON_TEST_FAIL_AT=plan makes a valid call fail as a HIP error would, before
+  // anything is enqueued (used by the host-side failure tests).
+  const char* v = std::getenv("DMUON_TEST_FAIL_AT");
+  if (v && std::strcmp(v, "plan") == 0) return fail(DMUON_E_HIP, "forced failure (DMUON_TEST_FAIL_AT=plan)");
+  return DMUON_OK;
+}
+
+}  // namespace dmuon
+
+using namespace dmuon;
+
+extern "C" {
+
+int32_t dmuon_abi_version(void) { return 1; }
+
+const char* dmuon_last_error(void) { return g_err.c_str(); }
+
+int dmuon_muon_step_workspace_size(const dmuon_tensor* tensors, int32_t n, const dmuon_step_cfg* cfg,
+                                   size_t* bytes) {
+  g_err.clear();
+  if (!bytes) return fail(DMUON_E_NULL, "bytes is NULL");
+  int e = check_cfg(cfg);
+  if (e) return e;
+  std::vector<Item> items;
+  if ((e = collect_items(tensors, n, items, nullptr))) return e;
+  if (items.empty()) {
+    *bytes = 0;
+    return DMUON_OK;
+  }
+  Plan pl;
+  if ((e = build_plan(items, cfg->prec == DMUON_PREC_F32, pl, nullptr))) return e;
+  *bytes = pl.bytes;
+  return DMUON_OK;
+}
+
+int dmuon_muon_step(const dmuon_tensor* tensors, int32_t n, const dmuon_step_cfg* cfg, void* workspace,
+                    size_t workspace_bytes, void* stream) {
+  g_err.clear();
+  int e = check_cfg(cfg);
+  if (e) return e;
+  std::vector<Item> items;
+  std::vector<Range> rs;
+  if ((e = collect_items(tensors, n, items, &rs))) return e;
+  if (items.empty()) return DMUON_OK;
+  if ((e = check_alias(rs))) return e;
+  const int f32 = cfg->prec == DMUON_PREC_F32;
+  Plan pl;
+  if ((e = build_plan(items, f32, pl, nullptr))) return e;
+  if ((e = check_workspace(workspace, workspace_bytes, pl.bytes))) return e;
+  const uintptr_t wlo = (uintptr_t)workspace, whi = wlo + pl.bytes;
+  for (const Range& r : rs)
+    if (r.lo < whi && wlo < r.hi) return fail(DMUON_E_ALIAS, "workspace overlaps a tensor buffer");
+  if ((e = test_fail_hook())) return e;
+  Plan real;
+  if ((e = build_plan(items, f32, real, (char*)workspace))) return e;
+  LaunchScalars s{};
+  s.mu = cfg->momentum;
+  s.lr = cfg->lr;
+  s.decay = (float)(1.0 - (double)cfg->lr * (double)cfg->weight_decay);
+  s.eps = cfg->eps;
+  s.a = cfg->a;
+  s.b = cfg->b;
+  s.c = cfg->c;
+  s.has_momentum = 1;
+  s.normalize = 1;
+  s.write_master = 1;
+  return run_plan(real, (char*)workspace, f32, s, cfg->ns_steps, stream);
+}
+
+int dmuon_ns_batched_workspace_size(int64_t batch, int64_t rows, int64_t cols, int32_t prec, int32_t steps,
+                                    size_t* bytes) {
+  g_err.clear();
+  if (!bytes) return fail(DMUON_E_NULL, "bytes is NULL");
+  if (prec != DMUON_PREC_BF16_MFMA && prec != DMUON_PREC_F32) return fail(DMUON_E_DTYPE, "unknown precision code");
+  if (steps < 0 || steps > kMaxSteps) return fail(DMUON_E_CFG, "steps must be in [0, 64]");
+  if (batch < 0 || rows < 0 || cols < 0) return fail(DMUON_E_SHAPE, "negative dim");
+  if (rows > 65536 || cols > 65536 || batch > (int64_t)1 << 30) return fail(DMUON_E_SHAPE, "dim too large");
+  if (batch * rows * cols == 0) {
+    *bytes = 0;
+    return DMUON_OK;
+  }
+  std::vector<Item> items{{batch, rows, cols, nullptr, 0, nullptr, nullptr, nullptr}};
+  Plan pl;
+  int e = build_plan(items, prec == DMUON_PREC_F32, pl, nullptr);
+  if (e) return e;
+  *bytes = pl.bytes;
+  return DMUON_OK;
+}
+
+int dmuon_ns_batched(const void* x, int32_t x_dtype, float* out, int64_t batch, int64_t rows, int64_t cols, float a,
+                     float b, float c, int32_t steps, float eps, int32_t normalize, int32_t prec, void* workspace,
+                     size_t workspace_bytes, void* stream) {
+  g_err.clear();
+  if (prec != DMUON_PREC_BF16_MFMA && prec != DMUON_PREC_F32) return fail(DMUON_E_DTYPE, "unknown precision code");
+  if (x_dtype != DMUON_F32 && x_dtype != DMUON_BF16) return fail(DMUON_E_DTYPE, "x_dtype must be DMUON_F32 or DMUON_BF16");
+  if (steps < 0 || steps > kMaxSteps) return fail(DMUON_E_CFG, "steps must be in [0, 64]");
+  if (!std::isfinite(eps) || eps < 0.f || !std::isfinite(a) || !std::isfinite(b) || !std::isfinite(c))
+    return fail(DMUON_E_CFG, "a, b, c, eps must be finite and eps >= 0");
+  if (normalize != 0 && normalize != 1) return fail(DMUON_E_CFG, "normalize must be 0 or 1");
+  if (batch < 0 || rows < 0 || cols < 0) return fail(DMUON_E_SHAPE, "negative dim");
+  if (rows > 65536 || cols > 65536 || batch > (int64_t)1 << 30) return fail(DMUON_E_SHAPE, "dim too large");
+  const int64_t numel = batch * rows * cols;
+  if (numel == 0) return DMUON_OK;
+  if (!x || !out) return fail(DMUON_E_NULL, "x and out must be set");
+  const size_t xs = x_dtype == DMUON_BF16 ? 2 : 4;
+  std::vector<Range> rs{{(uintptr_t)x, (uintptr_t)x + numel * xs, true},
+                        {(uintptr_t)out, (uintptr_t)out + numel * 4, false}};
+  int e = check_alias(rs);
+  if (e) return e;
+  std::vector<Item> items{{batch, rows, cols, x, x_dtype == DMUON_BF16, nullptr, nullptr, out}};
+  const int f32 = prec == DMUON_PREC_F32;
+  Plan pl;
+  if ((e = build_plan(items, f32, pl, nullptr))) return e;
+  if ((e = check_workspace(workspace, workspace_bytes, pl.bytes))) return e;
+  const uintptr_t wlo = (uintptr_t)workspace, whi = wlo + pl.bytes;
+  for (const Range& r : rs)
+    if (r.lo < whi && wlo < r.hi) return fail(DMUON_E_ALIAS, "workspace overlaps x or out");
+  if ((e = test_fail_hook())) return e;
+  Plan real;
+  if ((e = build_plan(items, f32, real, (char*)workspace))) return e;
+  LaunchScalars s{};
+  s.eps = eps;
+  s.a = a;
+  s.b = b;
+  s.c = c;
+  s.has_momentum = 0;
+  s.normalize = normalize;
+  s.write_master = 0;
+  return run_plan(real, (char*)workspace, f32, s, steps, stream);
+}
+
+int dmuon_gemm_nt(const void* A, const void* B, float* C, int64_t M, int64_t N, int64_t K, int64_t lda, int64_t ldb,
+                  int64_t ldc, int32_t dtype, void* stream) {
+  g_err.clear();
+  if (dtype != DMUON_F32 && dtype != DMUON_BF16) return fail(DMUON_E_DTYPE, "dtype must be DMUON_F32 or DMUON_BF16");
+  if (M < 0 || N < 0 || K < 0) return fail(DMUON_E_SHAPE, "negative dim");
+  if (M > INT32_MAX / 2 || N > INT32_MAX / 2) return fail(DMUON_E_SHAPE, "dim too large");
+  if (M == 0 || N == 0) return DMUON_OK;
+  if (!A || !B || !C) return fail(DMUON_E_NULL, "A, B and C must be set");
+  const int64_t kpad = round_up(K, kLdAlign);
+  if (lda % kLdAlign || ldb % kLdAlign || lda < kpad || ldb < kpad || ldc < N)
+    return fail(DMUON_E_SHAPE, "lda, ldb must be multiples of 64 and >= round_up(K, 64); ldc >= N");
+  if (((uintptr_t)A & 15) || ((uintptr_t)B & 15)) return fail(DMUON_E_SHAPE, "A and B must be 16-byte aligned");
+  if (K == 0) {
+    // the kernel still runs one K tile of (required zero) padding
+  }
+  const int r = launch_gemm_nt(A, B, C, M, N, K == 0 ? 1 : K, lda, ldb, ldc, dtype == DMUON_F32, stream);
+  if (r) return fail(DMUON_E_HIP, std::string("launch failed: ") + hip_error_string(r));
+  return DMUON_OK;
+}
+
+int dmuon_phase_timing(int32_t enable) {
+  std::lock_guard<std::mutex> lk(g_tmu);
+  g_timing = enable != 0;
+  return DMUON_OK;
+}
+
+int dmuon_phase_timing_read(double* ms, int64_t* count, int32_t n) {
+  g_err.clear();
+  if ((!ms || !count) && n > 0) return fail(DMUON_E_NULL, "ms and count must be set");
+  std::lock_guard<std::mutex> lk(g_tmu);
+  for (int i = 0; i < n; ++i) {
+    ms[i] = 0.0;
+    count[i] = 0;
+  }
+  int rc = DMUON_OK;
+  for (TimedLaunch& tl : g_timed) {
+    if (hipEventSynchronize(tl.b) != hipSuccess) rc = fail(DMUON_E_HIP, "event synchronize failed");
+    float t = 0.f;
+    if (rc == DMUON_OK && hipEventElapsedTime(&t, tl.a, tl.b) == hipSuccess && tl.phase < n) {
+      ms[tl.phase] += t;
+      count[tl.phase] += 1;
+    }
+    g_evpool.push_back(tl.a);
+    g_evpool.push_back(tl.b);
+  }
+  g_timed.clear();
+  return rc;
+}
+
+}  // extern "C"

@@ -1,0 +1,100 @@
+// Internal declarations shared by the host planner (plan.cpp, abi.cpp) and the
+// HIP kernels (kernels.hip).  Not part of the public ABI.
+#pragma once
+
+#include <cstddef>
+#include <cstdint>
+#include <string>
+
+namespace dmuon {
+
+// ---- tiling constants -------------------------------------------------------
+constexpr int kThreads = 256;          // threads per workgroup (4 wave64)
+constexpr int kTile = 256;             // output tile edge of the contraction kernels
+constexpr int kElemChunk = 16384;      // elements per workgroup of the momentum kernel
+constexpr int kPrepTile = 64;          // tile edge of the start (scale + copies) kernel
+constexpr int kLdAlign = 64;           // operand leading dims are multiples of this
+constexpr int kMaxSteps = 64;          // ns_steps upper bound
+constexpr int kScalStride = 80;        // floats of per-slice scalars (inv, d[0..k])
+
+enum Phase : int {
+  PH_MOMENTUM = 0,   // momentum + sum of squares
+  PH_START = 1,      // X0 = inv * B, operand copies
+  PH_GRAM = 2,       // A' = X Xᵀ − d I (upper tiles, mirrored)
+  PH_SQUARE = 3,     // B' = (b + 2cd) A' + c A'²
+  PH_APPLY = 4,      // X ← (a + bd + cd²) X + B' X (last: decay + update)
+  PH_UPDATE = 5,     // W ← (1 − lr wd) W − lr X0 (only when k = 0)
+  PH_GEMM = 6,       // test hook: plain NT product
+  PH_COUNT = 7
+};
+
+// One tensor (2-D = batch 1, or 3-D batch of slices) as the kernels see it.
+// All per-slice arrays are laid out slice after slice with the given strides
+// (in elements of the array's type).
+struct DevProblem {
+  int32_t batch, rows, cols;   // storage shape of one slice (row-major)
+  int32_t m, n;                // m = min(rows, cols), n = max
+  int32_t wide;                // 1: rows <= cols (Gram X Xᵀ on rows), 0: tall
+  int32_t ld_m;                // round_up(m, 64): ld of XA, A', B' (n×ld_m, m×ld_m)
+  int32_t ld_n;                // round_up(n, 64): ld of XG (m×ld_n)
+  int32_t grad_bf16;           // 1: grad is bf16, 0: fp32
+  int32_t chunks;              // momentum-kernel workgroups per slice
+  int32_t prep_tiles_r, prep_tiles_c;   // start-kernel 64×64 tiles per slice
+  int32_t tiles_m;             // ceil(m / 256)
+  int32_t apply_tr, apply_tc;  // apply tiles per slice over rows / cols of storage
+  int32_t slice_base;          // global index of this problem's first slice
+  int32_t pad0;
+  // per-phase workgroup prefix (first global workgroup of this problem)
+  int32_t wg0[PH_COUNT];
+  int32_t pad1;
+  // caller buffers (slice stride = rows*cols)
+  const void* grad;            // momentum-kernel input (grad, or x for ns_batched)
+  float* mom;                  // momentum (NULL for ns_batched)
+  float* master;               // master weight (NULL for ns_batched)
+  float* out;                  // NS output (NULL if not wanted)
+  // workspace (operand element type = bf16 or fp32 per precision)
+  float* xf;                   // fp32 iterate, storage layout, stride rows*cols
+  void* xg;                    // oriented X, m×ld_n, stride m*ld_n
+  void* xa0;                   // oriented Xᵀ, n×ld_m, stride n*ld_m (ping)
+  void* xa1;                   // (pong)
+  void* ap;                    // A', m×ld_m, stride m*ld_m
+  void* bp;                    // B', m×ld_m
+  float* part_norm;            // [batch][chunks]
+  float* part_apply;           // [batch][apply_tr*apply_tc]
+};
+
+// Scalars of one launch (passed by value).
+struct LaunchScalars {
+  float mu, lr, decay, eps;    // decay = 1 − lr·wd
+  float a, b, c;
+  int32_t t;                   // NS iteration index
+  int32_t last;                // 1 on the last apply
+  int32_t has_momentum;        // 0 for ns_batched
+  int32_t normalize;
+  int32_t write_master;
+};
+
+struct LaunchTable {
+  const DevProblem* probs;     // device
+  const int32_t* wg_prefix;    // device, [PH_COUNT][n_probs + 1]
+  float* scal;                 // device, [total_slices][kScalStride]
+  int32_t n_probs;
+  int32_t total_wg;            // workgroups of this launch
+};
+
+// Kernel launchers (kernels.hip).  Return 0 or a hipError_t value.
+int launch_phase(int phase, int prec_f32, const LaunchTable& tab, const LaunchScalars& s,
+                 void* stream);
+int launch_gemm_nt(const void* A, const void* B, float* C, int64_t M, int64_t N, int64_t K,
+                   int64_t lda, int64_t ldb, int64_t ldc, int f32, void* stream);
+const char* hip_error_string(int err);
+int upload_async(void* dst, const void* src, size_t bytes, void* stream);
+
+// Phase timing (abi.cpp).
+void timing_before(int phase, void* stream);
+void timing_after(int phase, void* stream);
+
+inline int64_t round_up(int64_t x, int64_t a) { return (x + a - 1) / a * a; }
+inline int64_t cdiv(int64_t x, int64_t a) { return (x + a - 1) / a; }
+
+}  // namespace dmuon

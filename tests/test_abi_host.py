@@ -1,0 +1,232 @@
+"""Host-side checks of libdmuon_ns that need no GPU.
+
+* the library loads and exports every function that include/dmuon_ns.h declares;
+* the C++ LPT equals the reference LPT of oracle/ (index work: bit-exact);
+* argument validation rejects every bad call before anything is enqueued (the
+  pointers used here are never dereferenced: validation makes no HIP call).
+"""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+from matrix_optimizer_muon_amd import _binding as B
+from matrix_optimizer_muon_amd import lpt_assign
+from oracle import lpt_assign as ref_lpt
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def header_functions():
+    text = open(os.path.join(ROOT, "include", "dmuon_ns.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(dmuon_[a-z_0-9]+)\s*\(", text)))
+
+
+def test_library_exports_every_header_function():
+    L = B.lib()
+    names = header_functions()
+    assert len(names) >= 10
+    for name in names:
+        assert hasattr(L, name), name
+    assert sorted(B.EXPORTED) == names
+    assert L.dmuon_abi_version() == 1
+
+
+# --------------------------------------------------------------------------
+# LPT: C++ == reference
+# --------------------------------------------------------------------------
+def compare_lpt(rows, cols, batch, layer, R, merge=0, kind=0, owner=0):
+    got = lpt_assign(rows, cols, batch, layer, R, merge_below_elems=merge, cost_kind=kind,
+                     owner_slot=owner)
+    want = ref_lpt(list(rows), list(cols), list(batch), list(layer), R, merge_below_elems=merge,
+                   cost_kind=kind, owner_slot=owner)
+    assert got["slot_of"].tolist() == want["slot_of"]
+    assert got["slot_load"].tolist() == want["slot_load"]
+    assert got["owner_order"].tolist() == want["owner_order"]
+    assert got["group_offsets"].tolist() == want["group_offsets"]
+    return got
+
+
+@pytest.mark.parametrize("seed", range(30))
+def test_lpt_matches_reference_random(seed):
+    rng = np.random.default_rng([31, seed])
+    n = int(rng.integers(1, 120))
+    R = int(rng.integers(1, 12))
+    rows = rng.choice([64, 128, 256, 512, 1000], n)
+    cols = rng.choice([64, 128, 256, 512, 1000], n)
+    batch = rng.integers(1, 4, n)
+    layer = rng.integers(-1, max(1, n // 5), n)
+    merge = int(rng.choice([0, 20000, 200000]))
+    compare_lpt(rows, cols, batch, layer, R, merge=merge, kind=int(seed % 2),
+                owner=int(rng.integers(0, R)))
+
+
+def test_lpt_matches_reference_llama_d4096():
+    from matrix_optimizer_muon_amd.workloads import workload
+    wl = workload("llama_d4096")
+    rows = [t.shape[0] for t in wl.tensors]
+    cols = [t.shape[1] for t in wl.tensors]
+    layer = [t.layer for t in wl.tensors]
+    for owner in range(8):
+        got = compare_lpt(rows, cols, [1] * 224, layer, 8, owner=owner)
+    assert got["slot_load"].max() / got["slot_load"].mean() < 1.03
+
+
+def test_lpt_empty_and_errors():
+    got = lpt_assign(np.zeros(0), np.zeros(0), np.zeros(0), np.zeros(0), 4)
+    assert got["slot_load"].tolist() == [0, 0, 0, 0]
+    assert got["owner_order"].tolist() == []
+    with pytest.raises(ValueError):
+        lpt_assign([1], [1], [1], [0], 0)
+    with pytest.raises(ValueError):
+        lpt_assign([1], [1], [0], [0], 2)            # batch must be >= 1
+    with pytest.raises(ValueError):
+        lpt_assign([1], [1], [1], [0], 2, owner_slot=2)
+
+
+# --------------------------------------------------------------------------
+# validation of the GPU entry points (no GPU needed: all calls are rejected)
+# --------------------------------------------------------------------------
+FAKE = 0x7f0000000000       # a plausible device address, never dereferenced
+
+
+def desc(ndim=2, shape=(8, 16), dtype=B.F32, base=FAKE, numel_bytes=1 << 20):
+    t = B.Tensor()
+    t.ndim = ndim
+    for i, s in enumerate(shape[:3]):
+        t.shape[i] = s
+    t.grad_dtype = dtype
+    t.grad = base
+    t.momentum = base + numel_bytes
+    t.master = base + 2 * numel_bytes
+    t.ns_out = None
+    return t
+
+
+def cfg(**kw):
+    c = dict(lr=0.02, momentum=0.95, weight_decay=0.01, eps=1e-7, coeffs=(3.4445, -4.775, 2.0315),
+             steps=5, precision="bf16")
+    c.update(kw)
+    return B.make_cfg(c["lr"], c["momentum"], c["weight_decay"], c["eps"], c["coeffs"],
+                      c["steps"], c["precision"])
+
+
+def step(descs, c=None, ws=FAKE + (1 << 40), ws_bytes=1 << 40):
+    arr = (B.Tensor * max(len(descs), 1))(*descs)
+    c = c or cfg()
+    return B.lib().dmuon_muon_step(arr, len(descs), ctypes.byref(c), ctypes.c_void_p(ws), ws_bytes,
+                                   None)
+
+
+def wsize(descs, c=None):
+    arr = (B.Tensor * max(len(descs), 1))(*descs)
+    out = ctypes.c_size_t(0)
+    rc = B.lib().dmuon_muon_step_workspace_size(arr, len(descs), ctypes.byref(c or cfg()),
+                                                ctypes.byref(out))
+    return rc, out.value
+
+
+def test_rejects_one_dim_tensor():
+    assert step([desc(ndim=1, shape=(128,))]) == -2
+    assert "2 dims" in B.lib().dmuon_last_error().decode()
+    assert step([desc(ndim=4, shape=(2, 3, 4))]) == -2
+
+
+def test_rejects_bad_arguments():
+    assert step([desc(shape=(-1, 4))]) == -3
+    assert step([desc(shape=(70000, 4))]) == -3
+    assert step([desc(dtype=7)]) == -4
+    assert step([desc()], cfg(precision="bf16"), ws=0) == -6
+    assert step([desc()], ws=FAKE + (1 << 40) + 8) == -6          # misaligned
+    assert step([desc()], ws_bytes=16) == -6                       # too small
+    assert step([desc()], cfg(steps=65)) == -5
+    assert step([desc()], cfg(steps=-1)) == -5
+    assert step([desc()], cfg(eps=-1.0)) == -5
+    assert step([desc()], cfg(lr=float("nan"))) == -5
+    bad = desc()
+    bad.master = None
+    assert step([bad]) == -1
+    c = cfg()
+    c.prec = 5
+    assert step([desc()], c) == -4
+    arr = (B.Tensor * 1)()
+    assert B.lib().dmuon_muon_step(arr, -1, ctypes.byref(cfg()), None, 0, None) == -3
+    assert B.lib().dmuon_muon_step(None, 1, ctypes.byref(cfg()), None, 0, None) == -1
+    assert B.lib().dmuon_muon_step(arr, 1, None, None, 0, None) == -1
+
+
+def test_rejects_aliasing():
+    a = desc()
+    a.master = a.momentum                                        # written twice
+    assert step([a]) == -7
+    a = desc()
+    a.ns_out = a.grad                                            # writes over the gradient
+    assert step([a]) == -7
+    x, y = desc(base=FAKE), desc(base=FAKE + (1 << 20))          # y.grad == x.momentum
+    assert step([x, y]) == -7
+    x, y = desc(base=FAKE), desc(base=FAKE)                      # shared grads only: allowed
+    y.momentum += 3 << 20
+    y.master += 3 << 20
+    rc, need = wsize([x, y])
+    assert rc == 0 and need > 0
+    # workspace overlapping a tensor
+    assert step([desc()], ws=FAKE, ws_bytes=1 << 40) == -7
+
+
+def test_zero_size_is_noop_and_needs_no_workspace():
+    assert step([desc(shape=(0, 16))], ws=0, ws_bytes=0) == 0
+    assert step([desc(ndim=3, shape=(0, 4, 4))], ws=0, ws_bytes=0) == 0
+    assert step([], ws=0, ws_bytes=0) == 0
+    assert wsize([desc(shape=(5, 0))]) == (0, 0)
+
+
+def test_workspace_size_properties():
+    rc1, s_bf = wsize([desc(shape=(256, 512))], cfg(precision="bf16"))
+    rc2, s_f = wsize([desc(shape=(256, 512))], cfg(precision="f32"))
+    assert rc1 == rc2 == 0
+    assert s_f > s_bf > 256 * 512 * 4
+    rc3, s_t = wsize([desc(shape=(512, 256))], cfg(precision="bf16"))   # tall: same operands
+    assert rc3 == 0 and s_t == s_bf
+    rc4, s_b = wsize([desc(ndim=3, shape=(3, 256, 512))], cfg(precision="bf16"))
+    assert rc4 == 0 and 2.5 * s_bf < s_b < 3.5 * s_bf
+    out = ctypes.c_size_t(0)
+    assert B.lib().dmuon_ns_batched_workspace_size(2, 100, 300, 0, 5, ctypes.byref(out)) == 0
+    assert out.value > 0
+    assert B.lib().dmuon_ns_batched_workspace_size(2, 100, 300, 9, 5, ctypes.byref(out)) == -4
+
+
+def test_ns_batched_and_gemm_validation():
+    L = B.lib()
+    vp = ctypes.c_void_p
+    args = dict(a=3.4445, b=-4.775, c=2.0315)
+    assert L.dmuon_ns_batched(vp(FAKE), 0, vp(FAKE), 1, 4, 4, *args.values(), 5, 1e-7, 1, 0,
+                              vp(0), 0, None) == -7                      # out overlaps x
+    assert L.dmuon_ns_batched(vp(FAKE), 0, vp(FAKE + 4096), 1, 4, 4, *args.values(), 5, 1e-7, 1,
+                              0, vp(0), 0, None) == -6
+    assert L.dmuon_ns_batched(vp(FAKE), 0, vp(FAKE + 8), 1, 4, 4, *args.values(), 5, 1e-7, 1, 0,
+                              vp(FAKE + (1 << 30)), 1 << 30, None) == -7
+    assert L.dmuon_ns_batched(vp(FAKE), 3, vp(FAKE), 1, 4, 4, *args.values(), 5, 1e-7, 1, 0,
+                              vp(0), 0, None) == -4
+    assert L.dmuon_ns_batched(vp(FAKE), 0, vp(FAKE + 4096), 1, 4, 4, *args.values(), 5, 1e-7, 2, 0,
+                              vp(0), 0, None) == -5
+    assert L.dmuon_ns_batched(None, 0, None, 0, 4, 4, *args.values(), 5, 1e-7, 1, 0,
+                              vp(0), 0, None) == 0
+    assert L.dmuon_gemm_nt(vp(FAKE), vp(FAKE), vp(FAKE), 4, 4, 10, 32, 64, 4, 1, None) == -3
+    assert L.dmuon_gemm_nt(vp(FAKE), vp(FAKE), vp(FAKE), 4, 4, 10, 64, 64, 4, 2, None) == -4
+
+
+def test_forced_failure_before_enqueue(monkeypatch):
+    monkeypatch.setenv("DMUON_TEST_FAIL_AT", "plan")
+    assert step([desc()]) == -8
+    assert "forced" in B.lib().dmuon_last_error().decode()
+    monkeypatch.delenv("DMUON_TEST_FAIL_AT")
+
+
+def test_python_wrappers_raise_value_error():
+    with pytest.raises(ValueError):
+        B.check(-2)
+    with pytest.raises(RuntimeError):
+        B.check(-8)

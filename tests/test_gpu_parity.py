@@ -1,0 +1,241 @@
+"""Parity of the HIP path against the fp64 oracle (needs an MI355X).
+
+Tolerances (relative Frobenius error, per tensor):
+* Newton–Schulz output O: ≤ 2e-2 on the bf16 matrix-core path, ≤ 1e-4 on the
+  fp32 path (the targets the workloads are defined with);
+* momentum B' = μB + G: ≤ 1e-6 against the oracle's fp64 value;
+* update W' against (1 − lr·wd)·W − lr·O evaluated in fp64 with the GPU's own O:
+  ≤ 1e-6 (the end-to-end W' error is the NS error times lr·‖O‖/‖W‖ and is
+  printed for information only).
+Shapes span several 256×256 tiles with ragged tails, wide and tall slices,
+batched 3-D tensors, bf16 and fp32 gradients and the degenerate sizes.
+"""
+import numpy as np
+import pytest
+
+torch = pytest.importorskip("torch")
+
+import matrix_optimizer_muon_amd as mm  # noqa: E402
+from matrix_optimizer_muon_amd.workloads import (HYPER, bf16_bits_to_f32, make_custom,  # noqa: E402
+                                                  make_tensor, workload)
+import oracle  # noqa: E402
+
+pytestmark = pytest.mark.gpu
+
+TOL_NS = {"bf16": 2e-2, "f32": 1e-4}
+Q5 = (HYPER["a"], HYPER["b"], HYPER["c"])
+
+
+def rel(x, y):
+    x = np.asarray(x, dtype=np.float64)
+    y = np.asarray(y, dtype=np.float64)
+    d = np.linalg.norm(y)
+    return np.linalg.norm(x - y) / (d if d > 0 else 1.0)
+
+
+def to_dev(td):
+    dev = "cuda"
+    if td.grad_bits is not None:
+        g = torch.from_numpy(td.grad_bits.view(np.int16).copy()).view(torch.bfloat16).to(dev)
+    else:
+        g = torch.from_numpy(td.grad.copy()).to(dev)
+    return (g, torch.from_numpy(td.momentum.copy()).to(dev),
+            torch.from_numpy(td.master.copy()).to(dev))
+
+
+def gpu_step(tds, precision, steps=5, want_o=True, hp=None):
+    hp = dict(HYPER, **(hp or {}))
+    devs = [to_dev(td) for td in tds]
+    outs = [torch.empty(td.grad.shape, dtype=torch.float32, device="cuda") for td in tds] \
+        if want_o else None
+    mm.muon_step([d[0] for d in devs], [d[1] for d in devs], [d[2] for d in devs],
+                 lr=hp["lr"], momentum=hp["mu"], weight_decay=hp["wd"], eps=hp["eps"],
+                 coeffs=(hp["a"], hp["b"], hp["c"]), steps=steps, precision=precision,
+                 ns_outs=outs)
+    torch.cuda.synchronize()
+    res = []
+    for i, d in enumerate(devs):
+        res.append((d[1].cpu().numpy(), None if outs is None else outs[i].cpu().numpy(),
+                    d[2].cpu().numpy()))
+    return res
+
+
+def check_step(tds, precision, steps=5, hp=None, label=""):
+    hp_full = dict(HYPER, **(hp or {}))
+    got = gpu_step(tds, precision, steps, hp=hp)
+    worst = 0.0
+    for td, (B1, O, W1) in zip(tds, got):
+        Bref, Oref, Wref = oracle.muon_step(td.grad, td.momentum, td.master, lr=hp_full["lr"],
+                                            mu=hp_full["mu"], wd=hp_full["wd"],
+                                            eps=hp_full["eps"], a=hp_full["a"], b=hp_full["b"],
+                                            c=hp_full["c"], steps=steps)
+        e_b = rel(B1, Bref)
+        e_o = rel(O, Oref)
+        w_from_o = oracle.decay_update(td.master, O, hp_full["lr"], hp_full["wd"])
+        e_w = rel(W1, w_from_o)
+        e_w_end = rel(W1, Wref)
+        print(f"{label} {td.spec.shape} {precision}: B {e_b:.2e} O {e_o:.2e} W {e_w:.2e} "
+              f"(end-to-end {e_w_end:.2e})", flush=True)
+        assert e_b <= 1e-6, (td.spec.shape, e_b)
+        assert e_o <= TOL_NS[precision], (td.spec.shape, e_o)
+        assert e_w <= 1e-6, (td.spec.shape, e_w)
+        worst = max(worst, e_o)
+    return worst
+
+
+# --------------------------------------------------------------------------
+# the contraction core alone
+# --------------------------------------------------------------------------
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("M,N,K", [(256, 256, 64), (300, 520, 200), (1, 1, 1), (513, 70, 1000),
+                                   (64, 1100, 130)])
+def test_gemm_nt_core(dtype, M, N, K):
+    rng = np.random.default_rng([41, M, N, K])
+    lda = ((K + 63) // 64) * 64
+    A = np.zeros((M, lda), np.float32)
+    Bm = np.zeros((N, lda), np.float32)
+    A[:, :K] = rng.standard_normal((M, K))
+    Bm[:, :K] = rng.standard_normal((N, K))
+    if dtype == "bf16":
+        from matrix_optimizer_muon_amd.workloads import f32_to_bf16_bits
+        ab, bb = f32_to_bf16_bits(A), f32_to_bf16_bits(Bm)
+        A, Bm = bf16_bits_to_f32(ab), bf16_bits_to_f32(bb)
+        Ad = torch.from_numpy(ab.view(np.int16).copy()).view(torch.bfloat16).cuda()
+        Bd = torch.from_numpy(bb.view(np.int16).copy()).view(torch.bfloat16).cuda()
+    else:
+        Ad, Bd = torch.from_numpy(A).cuda(), torch.from_numpy(Bm).cuda()
+    C = mm.gemm_nt(Ad, Bd, K).cpu().numpy()
+    ref = A.astype(np.float64) @ Bm.astype(np.float64).T
+    assert rel(C, ref) < 1e-5
+
+
+# --------------------------------------------------------------------------
+# Newton–Schulz alone
+# --------------------------------------------------------------------------
+NS_SHAPES = [(256, 512), (512, 256), (600, 1000), (1000, 600), (257, 257), (3, 96, 160),
+             (2, 160, 96), (1, 300), (300, 1), (1, 1), (64, 64), (130, 1500)]
+
+
+@pytest.mark.parametrize("precision", ["bf16", "f32"])
+@pytest.mark.parametrize("shape", NS_SHAPES)
+def test_ns_batched_parity(precision, shape):
+    td = make_custom(shape, "f32", seed=(51, len(shape) * 1000 + shape[-1]))
+    x = torch.from_numpy(td.grad.copy()).cuda()
+    out = mm.ns_batched(x, coeffs=Q5, steps=5, eps=HYPER["eps"], precision=precision)
+    torch.cuda.synchronize()
+    ref = oracle.newton_schulz_batched(td.grad, *Q5, 5, HYPER["eps"])
+    e = rel(out.cpu().numpy(), ref)
+    print(f"ns {shape} {precision}: {e:.2e}", flush=True)
+    assert e <= TOL_NS[precision]
+
+
+@pytest.mark.parametrize("precision", ["bf16", "f32"])
+def test_ns_bf16_input(precision):
+    td = make_custom((384, 700), "bf16", seed=(52, 0), scale=1e-3)
+    x = torch.from_numpy(td.grad_bits.view(np.int16).copy()).view(torch.bfloat16).cuda()
+    out = mm.ns_batched(x, precision=precision)
+    torch.cuda.synchronize()
+    ref = oracle.newton_schulz_batched(td.grad, *Q5, 5, HYPER["eps"])
+    assert rel(out.cpu().numpy(), ref) <= TOL_NS[precision]
+
+
+@pytest.mark.parametrize("precision", ["bf16", "f32"])
+def test_ns_cubic_fixed_point(precision):
+    rng = np.random.default_rng(53)
+    q, r = np.linalg.qr(rng.standard_normal((400, 400)))
+    Q = (q * np.sign(np.diag(r))[None, :])[:, :300].T.copy().astype(np.float32)   # 300×400
+    for X in (Q, Q.T.copy()):
+        out = mm.ns_batched(torch.from_numpy(X).cuda(), coeffs=(1.5, -0.5, 0.0), steps=3,
+                            normalize=False, precision=precision)
+        torch.cuda.synchronize()
+        e = rel(out.cpu().numpy(), X)
+        assert e <= TOL_NS[precision], e
+
+
+def test_ns_steps_zero_is_normalisation():
+    td = make_custom((100, 300), "f32", seed=(54, 0))
+    out = mm.ns_batched(torch.from_numpy(td.grad.copy()).cuda(), steps=0)
+    torch.cuda.synchronize()
+    ref = oracle.frobenius_normalize(td.grad, HYPER["eps"])
+    assert rel(out.cpu().numpy(), ref) < 1e-6
+
+
+# --------------------------------------------------------------------------
+# the whole step
+# --------------------------------------------------------------------------
+@pytest.mark.parametrize("precision", ["bf16", "f32"])
+def test_step_single_256x512(precision):
+    wl = workload("single_256x512")
+    td = make_tensor(wl, wl.tensors[0])
+    check_step([td], precision, label="single_256x512")
+
+
+@pytest.mark.parametrize("precision", ["bf16", "f32"])
+def test_step_mixed_group(precision):
+    """One grouped call over wide/tall, 2-D/3-D, bf16/fp32, ragged tensors."""
+    tds = [make_custom((600, 1000), "bf16", seed=(61, 0), scale=1e-3),
+           make_custom((1000, 600), "f32", seed=(61, 1)),
+           make_custom((3, 300, 520), "bf16", seed=(61, 2), scale=1e-3),
+           make_custom((2, 520, 300), "f32", seed=(61, 3)),
+           make_custom((257, 257), "f32", seed=(61, 4)),
+           make_custom((1, 700), "f32", seed=(61, 5)),
+           make_custom((0, 5), "f32", seed=(61, 6)),
+           make_custom((64, 64), "bf16", seed=(61, 7), scale=1e-3)]
+    check_step(tds, precision, label="mixed")
+
+
+@pytest.mark.parametrize("steps", [0, 1, 3])
+def test_step_other_k(steps):
+    tds = [make_custom((300, 700), "f32", seed=(62, steps)),
+           make_custom((700, 300), "bf16", seed=(62, 10 + steps), scale=1e-3)]
+    check_step(tds, "f32", steps=steps, label=f"k={steps}")
+    check_step(tds, "bf16", steps=steps, label=f"k={steps}")
+
+
+def test_step_zero_gradient():
+    td = make_custom((300, 500), "f32", seed=(63, 0), nonzero_momentum=False)
+    td.grad[:] = 0
+    (B1, O, W1), = gpu_step([td], "bf16")
+    assert np.all(B1 == 0) and np.all(O == 0)
+    assert rel(W1, (1 - HYPER["lr"] * HYPER["wd"]) * td.master.astype(np.float64)) < 1e-6
+
+
+def test_step_is_deterministic():
+    tds = [make_custom((700, 900), "bf16", seed=(64, 0), scale=1e-3),
+           make_custom((2, 300, 200), "f32", seed=(64, 1))]
+    a = gpu_step(tds, "bf16")
+    b = gpu_step(tds, "bf16")
+    for (b1, o1, w1), (b2, o2, w2) in zip(a, b):
+        assert np.array_equal(b1, b2) and np.array_equal(o1, o2) and np.array_equal(w1, w2)
+
+
+def test_step_resume_equals_two_steps():
+    """Two steps in a row equal one step, a host round trip of B and W, then another."""
+    td = make_custom((300, 640), "bf16", seed=(65, 0), scale=1e-3)
+    g, m, w = to_dev(td)
+    for _ in range(2):
+        mm.muon_step([g], [m], [w])
+    torch.cuda.synchronize()
+    g2, m2, w2 = to_dev(td)
+    mm.muon_step([g2], [m2], [w2])
+    torch.cuda.synchronize()
+    m3 = torch.from_numpy(m2.cpu().numpy()).cuda()
+    w3 = torch.from_numpy(w2.cpu().numpy()).cuda()
+    mm.muon_step([g2], [m3], [w3])
+    torch.cuda.synchronize()
+    assert torch.equal(m, m3) and torch.equal(w, w3)
+
+
+@pytest.mark.parametrize("precision", ["bf16"])
+def test_step_layer_d2048_full(precision):
+    """The one-layer d = 2048 workload at full size (7 matrices, one grouped launch)."""
+    wl = workload("layer_d2048")
+    tds = [make_tensor(wl, t) for t in wl.tensors]
+    check_step(tds, precision, label="layer_d2048")
+
+
+def test_step_merged_small_full():
+    """384 small matrices with a decaying spectrum in one grouped call (bf16 path)."""
+    wl = workload("merged_small")
+    tds = [make_tensor(wl, t) for t in wl.tensors]
+    check_step(tds, "bf16", label="merged_small")
