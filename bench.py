@@ -25,6 +25,51 @@ sys.path.insert(0, ROOT)
 PEAK_BF16_TFLOPS = 2500.0     # MI355X dense bf16 matrix-core peak (published)
 PEAK_HBM_GBS = 8000.0         # MI355X HBM3E (published)
 DEFAULT_WORKLOAD = "layer_d2048"
+METRIC = "Muon NS step matrices/s + TFLOP/s and % bf16 MFMA peak, 1\u00d7MI355X"
+KERNELS_SRC = os.path.join(ROOT, "matrix_optimizer_muon_amd", "csrc", "kernels.hip")
+PROFILES = os.path.join(ROOT, "profiles")
+
+
+def kernels_sha256():
+    import hashlib
+    with open(KERNELS_SRC, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()
+
+
+def measured_traffic(kernel, workload_name):
+    """HBM bytes per launch of ``kernel`` from the committed rocprofv3 counter summary.
+
+    The summary records FETCH_SIZE and WRITE_SIZE per dispatch, calibrated by the
+    same counters on a plain device copy of known size, and the sha256 of the
+    kernel source they were taken on; a different source gives None.
+    """
+    path = os.path.join(PROFILES, f"traffic_{kernel}_{workload_name}.md")
+    if not os.path.exists(path):
+        return None
+    fields = {}
+    with open(path) as f:
+        for line in f:
+            if ":" in line and line.strip().startswith("- "):
+                k, v = line.strip()[2:].split(":", 1)
+                fields[k.strip()] = v.strip().strip("`")
+    if fields.get("kernels_sha256") != kernels_sha256():
+        return None
+    try:
+        return float(fields["hbm_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def copy_probe(nbytes):
+    """A plain device-to-device copy of known size (counter calibration)."""
+    import torch
+    src = torch.empty(nbytes // 4, dtype=torch.float32, device="cuda").fill_(1.0)
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_probe_bytes": nbytes}), flush=True)
 
 
 def matrices_of(wl, share=None):
@@ -117,7 +162,12 @@ def main():
     ap.add_argument("--precision", default="bf16", choices=["bf16", "f32"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-phase-timing", action="store_true")
+    ap.add_argument("--copy-probe", type=int, default=0,
+                    help="only run a plain device copy of this many bytes (counter calibration)")
     args = ap.parse_args()
+    if args.copy_probe:
+        copy_probe(args.copy_probe)
+        return
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print("bench.py measures one GPU only: the owner-rank step has no cross-GPU work on its "
@@ -182,8 +232,10 @@ def main():
             ach = pf[dom] / (avg_ms * 1e-3) / 1e12
             roof = {"kernel": dom, "bound": "mfma", "achieved": round(ach, 2),
                     "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                    "frac": round(ach / PEAK_BF16_TFLOPS, 4), "traffic": None,
-                    "avg_launch_ms": round(avg_ms, 4), "flops_per_launch": pf[dom]}
+                    "frac": round(ach / PEAK_BF16_TFLOPS, 4),
+                    "traffic": measured_traffic(dom, args.workload),
+                    "avg_launch_ms": round(avg_ms, 4), "flops_per_launch": pf[dom],
+                    "launches": cnt}
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -194,7 +246,7 @@ def main():
     for t in ts:
         shapes[str(tuple(t.shape))] = shapes.get(str(tuple(t.shape)), 0) + 1
     line = {
-        "metric": "Muon NS step matrices/s (+ effective TFLOP/s and % bf16 dense MFMA peak), 1xMI355X",
+        "metric": METRIC,
         "value": round(slices / (ms_step * 1e-3), 3),
         "unit": "matrices/s",
         "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,

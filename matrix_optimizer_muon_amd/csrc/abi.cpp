@@ -139,13 +139,14 @@ static int build_plan(const std::vector<Item>& items, int prec_f32, Plan& pl, ch
     P.apply_tr = (int32_t)cdiv(it.rows, kTile);
     P.apply_tc = (int32_t)cdiv(it.cols, kTile);
     P.slice_base = (int32_t)slice_base;
+    P.ld_x = (int32_t)round_up(it.cols, 4);
     slice_base += it.batch;
     P.grad = it.grad;
     P.mom = it.mom;
     P.master = it.master;
     P.out = it.out;
     const int64_t b = it.batch;
-    P.xf = (float*)carve((size_t)(b * per) * 4);
+    P.xf = (float*)carve((size_t)(b * it.rows * P.ld_x) * 4);
     P.xg = carve((size_t)(b * P.m * P.ld_n) * esz);
     P.xa0 = carve((size_t)(b * P.n * P.ld_m) * esz);
     P.xa1 = carve((size_t)(b * P.n * P.ld_m) * esz);

@@ -43,7 +43,7 @@ struct DevProblem {
   int32_t tiles_m;             // ceil(m / 256)
   int32_t apply_tr, apply_tc;  // apply tiles per slice over rows / cols of storage
   int32_t slice_base;          // global index of this problem's first slice
-  int32_t pad0;
+  int32_t ld_x;                // round_up(cols, 4): ld of the fp32 iterate
   // per-phase workgroup prefix (first global workgroup of this problem)
   int32_t wg0[PH_COUNT];
   int32_t pad1;
@@ -53,7 +53,7 @@ struct DevProblem {
   float* master;               // master weight (NULL for ns_batched)
   float* out;                  // NS output (NULL if not wanted)
   // workspace (operand element type = bf16 or fp32 per precision)
-  float* xf;                   // fp32 iterate, storage layout, stride rows*cols
+  float* xf;                   // fp32 iterate, storage layout rows×ld_x, stride rows*ld_x
   void* xg;                    // oriented X, m×ld_n, stride m*ld_n
   void* xa0;                   // oriented Xᵀ, n×ld_m, stride n*ld_m (ping)
   void* xa1;                   // (pong)

@@ -59,13 +59,15 @@ template <> struct Op<float> {
 
 // Sum over the workgroup in a fixed order (xor butterfly inside each wave64,
 // then the four wave sums in a fixed tree): bit-identical on every run.
+template <int W>
 __device__ __forceinline__ float block_sum(float v, float* red) {
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
   const int w = threadIdx.x >> 6;
   if ((threadIdx.x & 63) == 0) red[w] = v;
   __syncthreads();
-  const float r = (red[0] + red[1]) + (red[2] + red[3]);
+  float r = (red[0] + red[1]) + (red[2] + red[3]);
+  if (W == 8) r += (red[4] + red[5]) + (red[6] + red[7]);
   __syncthreads();
   return r;
 }
@@ -80,10 +82,11 @@ __device__ __forceinline__ int find_prob(const int32_t* prefix, int n, int bid) 
 }
 
 // Σ of a slice's partials in a fixed order.
+template <int W>
 __device__ __forceinline__ float sum_partials(const float* part, int count, float* red) {
   float v = 0.f;
-  for (int i = threadIdx.x; i < count; i += kThreads) v += part[i];
-  return block_sum(v, red);
+  for (int i = threadIdx.x; i < count; i += 64 * W) v += part[i];
+  return block_sum<W>(v, red);
 }
 
 // ---------------------------------------------------------------------------
@@ -154,7 +157,7 @@ __global__ __launch_bounds__(kThreads) void k_momentum(LaunchTable tab, LaunchSc
     }
     acc = fmaf(x, x, acc);
   }
-  const float tot = block_sum(acc, red);
+  const float tot = block_sum<4>(acc, red);
   if (threadIdx.x == 0) P.part_norm[(int64_t)slice * P.chunks + chunk] = tot;
 }
 
@@ -176,7 +179,7 @@ __global__ __launch_bounds__(kThreads) void k_start(LaunchTable tab, LaunchScala
   const int r0 = (tt / P.prep_tiles_c) * kPrepTile, c0 = (tt % P.prep_tiles_c) * kPrepTile;
   const int rows = P.rows, cols = P.cols;
 
-  const float total = sum_partials(P.part_norm + (int64_t)slice * P.chunks, P.chunks, red);
+  const float total = sum_partials<4>(P.part_norm + (int64_t)slice * P.chunks, P.chunks, red);
   const float inv = s.normalize ? 1.0f / (sqrtf(total) + s.eps) : 1.0f;
   float* scal = tab.scal + (int64_t)(P.slice_base + slice) * kScalStride;
   if (tt == 0 && threadIdx.x == 0) {
@@ -189,7 +192,7 @@ __global__ __launch_bounds__(kThreads) void k_start(LaunchTable tab, LaunchScala
                                      : (P.grad_bf16 ? nullptr : (const float*)P.grad + (int64_t)slice * per);
   const uint16_t* srcb = (!s.has_momentum && P.grad_bf16) ? (const uint16_t*)P.grad + (int64_t)slice * per
                                                           : nullptr;
-  float* xf = P.xf + (int64_t)slice * per;
+  float* xf = P.xf + (int64_t)slice * rows * P.ld_x;
   const int ld_s = P.wide ? P.ld_n : P.ld_m;    // straight copy: cols padded
   const int ld_t = P.wide ? P.ld_m : P.ld_n;    // transposed copy: rows padded
   T* cs = (T*)(P.wide ? P.xg : P.xa0) + (int64_t)slice * rows * ld_s;
@@ -209,7 +212,7 @@ __global__ __launch_bounds__(kThreads) void k_start(LaunchTable tab, LaunchScala
       if (r < rows && c < cols) {
         const int64_t o = (int64_t)r * cols + c;
         x = (srcb ? bf16_to_f32(srcb[o]) : srcf[o]) * inv;
-        xf[o] = x;
+        xf[(int64_t)r * P.ld_x + c] = x;
       }
       v[e] = x;
       tile[lr][tc + e] = x;
@@ -247,131 +250,223 @@ __global__ __launch_bounds__(kThreads) void k_update(LaunchTable tab, LaunchScal
   const int slice = local / P.chunks, chunk = local % P.chunks;
   const int64_t per = (int64_t)P.rows * P.cols;
   const int64_t base = (int64_t)slice * per;
+  const float* xf = P.xf + (int64_t)slice * P.rows * P.ld_x;
   const int64_t e0 = (int64_t)chunk * kElemChunk;
   const int64_t e1 = (e0 + kElemChunk < per) ? e0 + kElemChunk : per;
   for (int64_t e = e0 + threadIdx.x; e < e1; e += kThreads) {
-    const float x = P.xf[base + e];
+    const int64_t r = e / P.cols, c = e - r * P.cols;
+    const float x = xf[r * P.ld_x + c];
     if (P.out) P.out[base + e] = x;
     if (s.write_master) P.master[base + e] = fmaf(-s.lr, x, s.decay * P.master[base + e]);
   }
 }
 
 // ---------------------------------------------------------------------------
-// NT contraction core on the matrix cores: 256×256 output tile, 4 waves in a
-// 2×2 grid of 128×128 wave tiles (4×4 blocks of 32×32), K staged through LDS in
-// 128-byte rows (64 bf16 or 32 fp32), double buffered; 16-byte chunks of each
-// LDS row are XOR-swizzled by (row & 7) so that ds_read_b128 of 32 rows and the
-// row-contiguous ds_write_b128 are both bank-conflict free.
+// NT contraction core on the matrix cores.
+//
+// One workgroup = 8 wave64s (two per SIMD) computing a 256×256 output tile; each
+// wave owns a 128×64 sub-tile (4×2 blocks of 32×32 MFMA output).  K is staged
+// through LDS in 64-byte rows (32 bf16 or 16 fp32 per row and stage), four stages
+// deep, filled by buffer_load … lds (global → LDS without VGPRs; rows beyond the
+// operand read as zero through the buffer's range check).  The four 16-byte
+// chunks of a row are XOR-swizzled with (row >> 2) & 3 so that 16 consecutive
+// rows read at one logical chunk cover all 64 LDS banks.  Per stage: fragment
+// reads of the second half-step overlap the first half-step's MFMAs, then one
+// barrier hands over the next stage and its first fragments are read while the
+// second half-step's MFMAs run.
 // ---------------------------------------------------------------------------
-constexpr int kLdsRow = 128;                          // bytes per staged row
-constexpr int kStageBytes = 2 * kTile * kLdsRow;      // A + B rows of one stage
-constexpr int kGemmLds = 2 * kStageBytes;             // double buffered: 128 KiB
+constexpr int kGemmWaves = 8;
+constexpr int kGemmThreads = 64 * kGemmWaves;
+constexpr int kRowBytes = 64;                          // staged bytes per operand row
+constexpr int kStageBytes = 2 * kTile * kRowBytes;     // A rows + B rows: 32 KiB
+constexpr int kStages = 4;
+constexpr int kGemmLds = kStages * kStageBytes;        // 128 KiB
+constexpr int kDmaPerStage = 4;                        // buffer_load … lds per thread per stage
+static_assert(kTile == 256 && kGemmWaves == 8, "fragment layout assumes 8 waves on a 256 tile");
+
+typedef unsigned u32x4_t __attribute__((ext_vector_type(4)));
 
 struct Operands {
-  const char* a;     // first row of the tile's A rows (bytes)
-  const char* b;
-  int64_t lda_b;     // leading dims in bytes
-  int64_t ldb_b;
-  int rows_a;        // valid A rows from the tile start (≤ 0: none)
+  const char* a;     // first A row of the tile
+  const char* b;     // first B row of the tile
+  int lda_b;         // leading dims in bytes (multiples of 128)
+  int ldb_b;
+  int rows_a;        // valid rows from the tile start
   int rows_b;
-  int ktiles;        // K / (elements per 128-byte row)
+  int ktiles;        // K bytes per row / 64
 };
 
 template <typename T>
-__device__ __forceinline__ void mfma_chunk(f32x16_t& acc, const uint4& a, const uint4& b);
+__device__ __forceinline__ void mfma_chunk(f32x16_t& acc, const u32x4_t& a, const u32x4_t& b);
 
 template <>
-__device__ __forceinline__ void mfma_chunk<uint16_t>(f32x16_t& acc, const uint4& a, const uint4& b) {
+__device__ __forceinline__ void mfma_chunk<uint16_t>(f32x16_t& acc, const u32x4_t& a, const u32x4_t& b) {
   bf16x8_t va, vb;
   __builtin_memcpy(&va, &a, 16);
   __builtin_memcpy(&vb, &b, 16);
   acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, vb, acc, 0, 0, 0);
 }
 
-// fp32: the 16-byte chunk holds 4 consecutive k; element e of the lanes of both
-// halves forms one K=2 step.  A and B use the same k permutation, so the sum
-// over k is the same set of products.
+// fp32: a 16-byte chunk holds 4 consecutive k; element e of the two lane halves
+// forms one K = 2 step.  A and B use the same k permutation, so the sum covers
+// the same products.
 template <>
-__device__ __forceinline__ void mfma_chunk<float>(f32x16_t& acc, const uint4& a, const uint4& b) {
+__device__ __forceinline__ void mfma_chunk<float>(f32x16_t& acc, const u32x4_t& a, const u32x4_t& b) {
   acc = __builtin_amdgcn_mfma_f32_32x32x2f32(__uint_as_float(a.x), __uint_as_float(b.x), acc, 0, 0, 0);
   acc = __builtin_amdgcn_mfma_f32_32x32x2f32(__uint_as_float(a.y), __uint_as_float(b.y), acc, 0, 0, 0);
   acc = __builtin_amdgcn_mfma_f32_32x32x2f32(__uint_as_float(a.z), __uint_as_float(b.z), acc, 0, 0, 0);
   acc = __builtin_amdgcn_mfma_f32_32x32x2f32(__uint_as_float(a.w), __uint_as_float(b.w), acc, 0, 0, 0);
 }
 
-template <typename T>
-__device__ __forceinline__ void gemm_mainloop(const Operands& op, char* smem, f32x16_t (&acc)[4][4]) {
-  const int tid = threadIdx.x;
-  const int lrow = tid >> 3;                 // 0..31, + 32·q
-  const int chunk = tid & 7;
-  const int sw = (chunk ^ (lrow & 7)) * 16;  // swizzled byte offset inside a row
-  uint4 ra[8], rb[8];
+// s_waitcnt with only vmcnt constrained (expcnt 7, lgkmcnt 15 = no wait)
+#define DMUON_WAIT_VM(n) __builtin_amdgcn_s_waitcnt((0x7 << 4) | (0xF << 8) | ((n) & 15) | ((((n) >> 4) & 3) << 14))
 
+template <typename T>
+__device__ __forceinline__ void gemm_mainloop(const Operands& op, char* smem, f32x16_t (&acc)[4][2]) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wr = wave >> 2, wc = wave & 3, h = lane >> 5, r32 = lane & 31;
+  const __amdgpu_buffer_rsrc_t ra = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)op.a, 0, (op.rows_a < kTile ? op.rows_a : kTile) * op.lda_b, 0x00020000);
+  const __amdgpu_buffer_rsrc_t rb = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)op.b, 0, (op.rows_b < kTile ? op.rows_b : kTile) * op.ldb_b, 0x00020000);
+  // DMA: wave w fills rows [32w, 32w + 32) of A and of B, 16 rows per instruction;
+  // lane l lands at byte 16·l of the instruction's 1 KiB = row l/4, physical chunk l%4.
+  int offa[2], offb[2];
+#pragma unroll
+  for (int q = 0; q < 2; ++q) {
+    const int row = (wave * 2 + q) * 16 + (lane >> 2);
+    const int c = (lane & 3) ^ ((row >> 2) & 3);
+    offa[q] = row * op.lda_b + c * 16;
+    offb[q] = row * op.ldb_b + c * 16;
+  }
+  // fragment offsets inside a stage for logical chunk 2·ss + h
+  int fa_off[2][4], fb_off[2][2];
+#pragma unroll
+  for (int ss = 0; ss < 2; ++ss) {
+    const int c = 2 * ss + h;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int row = wr * 128 + i * 32 + r32;
+      fa_off[ss][i] = row * kRowBytes + ((c ^ ((row >> 2) & 3)) * 16);
+    }
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const int row = wc * 64 + j * 32 + r32;
+      fb_off[ss][j] = kTile * kRowBytes + row * kRowBytes + ((c ^ ((row >> 2) & 3)) * 16);
+    }
+  }
 #pragma unroll
   for (int i = 0; i < 4; ++i)
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
+    for (int j = 0; j < 2; ++j)
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
 
-  auto gload = [&](int kt) {
-    const int64_t koff = (int64_t)kt * kLdsRow + chunk * 16;
+  u32x4_t fa[2][4], fb[2][2];
+  auto issue = [&](int kt) {
+    char* base = smem + (kt % kStages) * kStageBytes;
 #pragma unroll
-    for (int q = 0; q < 8; ++q) {
-      const int row = lrow + 32 * q;
-      ra[q] = row < op.rows_a ? *(const uint4*)(op.a + row * op.lda_b + koff) : make_uint4(0, 0, 0, 0);
-      rb[q] = row < op.rows_b ? *(const uint4*)(op.b + row * op.ldb_b + koff) : make_uint4(0, 0, 0, 0);
+    for (int q = 0; q < 2; ++q) {
+      char* da = base + (wave * 2 + q) * 16 * kRowBytes;
+      char* db = da + kTile * kRowBytes;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (__attribute__((address_space(3))) void*)da, 16,
+                                               offa[q] + kt * kRowBytes, 0, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, (__attribute__((address_space(3))) void*)db, 16,
+                                               offb[q] + kt * kRowBytes, 0, 0, 0);
     }
   };
-  auto lstore = [&](int stage) {
-    char* sa = smem + stage * kStageBytes;
-    char* sb = sa + kTile * kLdsRow;
+  auto fload = [&](int kt, int ss, int buf) {
+    const char* base = smem + (kt % kStages) * kStageBytes;
 #pragma unroll
-    for (int q = 0; q < 8; ++q) {
-      const int row = lrow + 32 * q;
-      *(uint4*)(sa + row * kLdsRow + sw) = ra[q];
-      *(uint4*)(sb + row * kLdsRow + sw) = rb[q];
-    }
+    for (int i = 0; i < 4; ++i) fa[buf][i] = *(const u32x4_t*)(base + fa_off[ss][i]);
+#pragma unroll
+    for (int j = 0; j < 2; ++j) fb[buf][j] = *(const u32x4_t*)(base + fb_off[ss][j]);
+  };
+  auto mmas = [&](int buf) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 2; ++j) mfma_chunk<T>(acc[i][j], fa[buf][i], fb[buf][j]);
   };
 
-  const int lane = tid & 63, wave = tid >> 6;
-  const int wr = wave >> 1, wc = wave & 1;
-  const int h = lane >> 5, r32 = lane & 31;
-
-  gload(0);
-  lstore(0);
-  __syncthreads();
-  for (int kt = 0; kt < op.ktiles; ++kt) {
-    const bool more = kt + 1 < op.ktiles;
-    if (more) gload(kt + 1);
-    const char* sa = smem + (kt & 1) * kStageBytes;
-    const char* sb = sa + kTile * kLdsRow;
+  const int KT = op.ktiles;
 #pragma unroll
-    for (int ss = 0; ss < 4; ++ss) {
-      const int off = ((2 * ss + h) ^ (r32 & 7)) * 16;
-      uint4 fa[4], fb[4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) fa[i] = *(const uint4*)(sa + (wr * 128 + i * 32 + r32) * kLdsRow + off);
-#pragma unroll
-      for (int j = 0; j < 4; ++j) fb[j] = *(const uint4*)(sb + (wc * 128 + j * 32 + r32) * kLdsRow + off);
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) mfma_chunk<T>(acc[i][j], fa[i], fb[j]);
+  for (int s = 0; s < kStages - 1; ++s)
+    if (s < KT) issue(s);
+  if (kStages - 2 < KT) DMUON_WAIT_VM(kDmaPerStage * (kStages - 2));
+  else DMUON_WAIT_VM(0);
+  __builtin_amdgcn_s_barrier();
+  fload(0, 0, 0);
+  for (int kt = 0; kt < KT; ++kt) {
+    fload(kt, 1, 1);
+    __builtin_amdgcn_sched_barrier(0);
+    mmas(0);
+    __builtin_amdgcn_sched_barrier(0);
+    if (kt + 1 < KT) {
+      // stage kt+1 landed for every wave, and every wave is done reading stage kt-1
+      if (kt + kStages - 2 < KT) DMUON_WAIT_VM(kDmaPerStage * (kStages - 3));
+      else DMUON_WAIT_VM(0);
+      __builtin_amdgcn_s_barrier();
+      if (kt + kStages - 1 < KT) issue(kt + kStages - 1);
+      fload(kt + 1, 0, 0);
     }
-    if (more) lstore((kt + 1) & 1);
-    __syncthreads();
+    __builtin_amdgcn_sched_barrier(0);
+    mmas(1);
+    __builtin_amdgcn_sched_barrier(0);
   }
+  // all LDS reads done before the caller reuses LDS
+  __syncthreads();
 }
 
 // Position of accumulator register r of block (i, j) inside the 256×256 tile.
-__device__ __forceinline__ int acc_row(int i, int r) {
+__device__ __forceinline__ int acc_row(int i, int rq) {   // rq = r >> 2; rows rq·8 + h·4 + 0..3
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  return (wave >> 1) * 128 + i * 32 + (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3);
+  return (wave >> 2) * 128 + i * 32 + rq * 8 + (lane >> 5) * 4;
 }
 __device__ __forceinline__ int acc_col(int j) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  return (wave & 1) * 128 + j * 32 + (lane & 31);
+  return (wave & 3) * 64 + j * 32 + (lane & 31);
+}
+
+// Store 4 consecutive elements (rows gr0..gr0+3 of the tile, one column) as one
+// vector into a transposed row: dst[col][gr0 .. gr0+3].
+__device__ __forceinline__ void store4(uint16_t* p, float a, float b, float c, float d) {
+  const uint32_t lo = (uint32_t)f32_to_bf16(a) | ((uint32_t)f32_to_bf16(b) << 16);
+  const uint32_t hi = (uint32_t)f32_to_bf16(c) | ((uint32_t)f32_to_bf16(d) << 16);
+  *(uint2*)p = make_uint2(lo, hi);
+}
+__device__ __forceinline__ void store4(float* p, float a, float b, float c, float d) {
+  *(float4*)p = make_float4(a, b, c, d);
+}
+
+// Byte offset of element (r, c) of a staged 128×256 fp32 half-tile: 1 KiB rows,
+// 16-byte chunks XOR-swizzled by (r >> 3) & 15 so that row-contiguous 16-byte
+// reads and reads of one column over 16 row groups both spread over all banks.
+__device__ __forceinline__ int stage_off(int r, int c) {
+  return r * 1024 + ((((c >> 2) ^ ((r >> 3) & 15)) << 4) | ((c & 3) << 2));
+}
+
+__device__ __forceinline__ void load4(const uint16_t* p, float (&v)[4]) {
+  const uint2 u = *(const uint2*)p;
+  v[0] = __uint_as_float(u.x << 16); v[1] = __uint_as_float(u.x & 0xffff0000u);
+  v[2] = __uint_as_float(u.y << 16); v[3] = __uint_as_float(u.y & 0xffff0000u);
+}
+__device__ __forceinline__ void load4(const float* p, float (&v)[4]) {
+  const float4 u = *(const float4*)p;
+  v[0] = u.x; v[1] = u.y; v[2] = u.z; v[3] = u.w;
+}
+
+// 16 bytes of one destination row: 8 bf16 or 4 fp32 values
+__device__ __forceinline__ void store_row16(uint16_t* p, const float (&v)[8]) {
+  uint4 u;
+  u.x = (uint32_t)f32_to_bf16(v[0]) | ((uint32_t)f32_to_bf16(v[1]) << 16);
+  u.y = (uint32_t)f32_to_bf16(v[2]) | ((uint32_t)f32_to_bf16(v[3]) << 16);
+  u.z = (uint32_t)f32_to_bf16(v[4]) | ((uint32_t)f32_to_bf16(v[5]) << 16);
+  u.w = (uint32_t)f32_to_bf16(v[6]) | ((uint32_t)f32_to_bf16(v[7]) << 16);
+  *(uint4*)p = u;
+}
+__device__ __forceinline__ void store_row16(float* p, const float (&v)[4]) {
+  *(float4*)p = make_float4(v[0], v[1], v[2], v[3]);
 }
 
 // upper-triangle tile u (row-major over ti ≤ tj) of a T×T tile grid
@@ -382,17 +477,25 @@ __device__ __forceinline__ void tri_tile(int u, int T, int& ti, int& tj) {
   tj = i + (u - start);
 }
 
+// Logical workgroup index: workgroups are handed to the 8 XCDs round-robin, so
+// give each XCD one contiguous range of logical tiles (they share operand panels
+// in that XCD's L2).
+__device__ __forceinline__ int xcd_logical_block() {
+  const int G = gridDim.x, b = blockIdx.x;
+  const int xcd = b & 7, local = b >> 3, per = G >> 3, rem = G & 7;
+  return (xcd < rem ? xcd * (per + 1) : rem * (per + 1) + (xcd - rem) * per) + local;
+}
+
 template <typename T, int PH>
-__global__ __launch_bounds__(kThreads, 1) void k_gemm(LaunchTable tab, LaunchScalars s) {
+__global__ __launch_bounds__(kGemmThreads) void k_gemm(LaunchTable tab, LaunchScalars s) {
   extern __shared__ __align__(16) char smem[];
-  __shared__ float red[4];
-  constexpr int kElemsPerRow = kLdsRow / (int)sizeof(T);
-  const int bid = blockIdx.x;
+  __shared__ float red[kGemmWaves];
+  constexpr int kElemsPerRow = kRowBytes / (int)sizeof(T);
+  const int bid = xcd_logical_block();
   const int p = find_prob(tab.wg_prefix + PH * (tab.n_probs + 1), tab.n_probs, bid);
   const DevProblem& P = tab.probs[p];
   const int local = bid - P.wg0[PH];
   const int m = P.m;
-  float* scal_base = tab.scal;
 
   Operands op;
   int slice, row0, col0, ti = 0, tj = 0, u;
@@ -409,123 +512,199 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm(LaunchTable tab, LaunchSca
                                   : (const T*)P.ap + (int64_t)slice * m * P.ld_m;
     op.a = (const char*)(base + (int64_t)row0 * ld);
     op.b = (const char*)(base + (int64_t)col0 * ld);
-    op.lda_b = op.ldb_b = (int64_t)ld * sizeof(T);
+    op.lda_b = op.ldb_b = ld * (int)sizeof(T);
     op.rows_a = m - row0;
     op.rows_b = m - col0;
     op.ktiles = ld / kElemsPerRow;
-  } else {  // PH_APPLY
+  } else {  // PH_APPLY: tiles ordered with the long (n) dimension outermost
     const int per = P.apply_tr * P.apply_tc;
     slice = local / per;
     u = local % per;
-    row0 = (u / P.apply_tc) * kTile;
-    col0 = (u % P.apply_tc) * kTile;
+    int tr, tc;
+    if (P.wide) { tc = u / P.apply_tr; tr = u % P.apply_tr; }
+    else { tr = u / P.apply_tc; tc = u % P.apply_tc; }
+    u = tr * P.apply_tc + tc;           // partial-sum slot in row-major tile order
+    row0 = tr * kTile;
+    col0 = tc * kTile;
     const T* bp = (const T*)P.bp + (int64_t)slice * m * P.ld_m;
     const T* xa = (const T*)((s.t & 1) ? P.xa1 : P.xa0) + (int64_t)slice * P.n * P.ld_m;
     const T* pa = P.wide ? bp : xa;     // rows of the output = storage rows
     const T* pb = P.wide ? xa : bp;     // cols of the output = storage cols
     op.a = (const char*)(pa + (int64_t)row0 * P.ld_m);
     op.b = (const char*)(pb + (int64_t)col0 * P.ld_m);
-    op.lda_b = op.ldb_b = (int64_t)P.ld_m * sizeof(T);
+    op.lda_b = op.ldb_b = P.ld_m * (int)sizeof(T);
     op.rows_a = P.rows - row0;
     op.rows_b = P.cols - col0;
     op.ktiles = P.ld_m / kElemsPerRow;
   }
-  float* scal = scal_base + (int64_t)(P.slice_base + slice) * kScalStride;
+  float* scal = tab.scal + (int64_t)(P.slice_base + slice) * kScalStride;
 
   // d_t: at t = 0 from the start kernel; later the sum of the previous apply's
   // per-tile Σ X² partials (fixed order, identical in every workgroup).
   float d;
   if (PH == PH_GRAM && s.t > 0) {
     const int cnt = P.apply_tr * P.apply_tc;
-    d = sum_partials(P.part_apply + (int64_t)slice * cnt, cnt, red) / (float)m;
+    d = sum_partials<kGemmWaves>(P.part_apply + (int64_t)slice * cnt, cnt, red) / (float)m;
     if (u == 0 && threadIdx.x == 0) scal[1 + s.t] = d;
   } else {
     d = scal[1 + s.t];
   }
 
-  f32x16_t acc[4][4];
+  f32x16_t acc[4][2];
   gemm_mainloop<T>(op, smem, acc);
 
+  // ---- epilogue: each 128-row half of the tile is staged in LDS (fp32), then a
+  // row pass does the row-major global I/O with 16-byte vectors and a column pass
+  // writes the transposed copy (apply) or the mirrored block (Gram, square).
+  const int tid = threadIdx.x;
+  const int ldm = P.ld_m;
+  T* dst = nullptr;            // row-major destination (Gram: A', square: B', apply: straight copy)
+  T* dstT = nullptr;           // transposed destination (mirror / transposed copy)
+  int ld_dst = 0, ld_t = 0, rows_lim = 0, cols_lim = 0, ldst_lim = 0, t_rows_lim = 0;
+  const T* aprime = nullptr;
+  float alpha = 0.f, lin = 0.f;
+  const int rows = P.rows, cols = P.cols;
+  float* xf = nullptr;
+  float* wst = nullptr;
+  float* outp = nullptr;
+  bool vec_user = false;
   if (PH == PH_GRAM || PH == PH_SQUARE) {
-    T* dst = (T*)(PH == PH_GRAM ? P.ap : P.bp) + (int64_t)slice * m * P.ld_m;
-    const T* aprime = (const T*)P.ap + (int64_t)slice * m * P.ld_m;
-    const float lin = s.b + 2.f * s.c * d;
-    const int ldm = P.ld_m;
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int gc = col0 + acc_col(j);
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int gr = row0 + acc_row(i, r);
-          float v = acc[i][j][r];
-          if (PH == PH_GRAM) {
-            if (gr == gc && gr < m) v -= d;
-          } else {
-            const float ap = (gr < m && gc < ldm) ? Op<T>::to(aprime[(int64_t)gr * ldm + gc]) : 0.f;
-            v = fmaf(lin, ap, s.c * v);
-          }
-          const T tv = Op<T>::from(v);
-          if (gr < m && gc < ldm) dst[(int64_t)gr * ldm + gc] = tv;
-          if (ti != tj && gc < m && gr < ldm) dst[(int64_t)gc * ldm + gr] = tv;
-        }
-      }
-  } else {  // PH_APPLY
-    const float alpha = s.a + s.b * d + s.c * d * d;
-    const int rows = P.rows, cols = P.cols;
-    const int64_t per = (int64_t)rows * cols;
-    float* xf = P.xf + (int64_t)slice * per;
-    float acc_sq = 0.f;
+    dst = (T*)(PH == PH_GRAM ? P.ap : P.bp) + (int64_t)slice * m * ldm;
+    dstT = ti != tj ? dst : nullptr;
+    ld_dst = ld_t = ldm;
+    rows_lim = m;          // valid output rows
+    cols_lim = m;          // valid output cols (values beyond are zero)
+    ldst_lim = ldm;        // columns written (zero padding up to ld)
+    t_rows_lim = m;        // rows of the transposed destination
+    aprime = (const T*)P.ap + (int64_t)slice * m * ldm;
+    lin = s.b + 2.f * s.c * d;
+  } else {
+    alpha = s.a + s.b * d + s.c * d * d;
+    xf = P.xf + (int64_t)slice * rows * P.ld_x;
+    rows_lim = rows;
+    cols_lim = cols;
     if (s.last) {
-      float* out = P.out ? P.out + (int64_t)slice * per : nullptr;
-      float* w = s.write_master ? P.master + (int64_t)slice * per : nullptr;
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const int gc = col0 + acc_col(j);
-          if (gc >= cols) continue;
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int gr = row0 + acc_row(i, r);
-            if (gr >= rows) continue;
-            const int64_t o = (int64_t)gr * cols + gc;
-            const float xn = fmaf(alpha, xf[o], acc[i][j][r]);
-            if (out) out[o] = xn;
-            if (w) w[o] = fmaf(-s.lr, xn, s.decay * w[o]);
-          }
-        }
+      const int64_t per = (int64_t)rows * cols;
+      wst = s.write_master ? P.master + (int64_t)slice * per : nullptr;
+      outp = P.out ? P.out + (int64_t)slice * per : nullptr;
+      vec_user = (cols & 3) == 0 && (!wst || ((uintptr_t)wst & 15) == 0) &&
+                 (!outp || ((uintptr_t)outp & 15) == 0);
     } else {
       const int ld_s = P.wide ? P.ld_n : P.ld_m;
-      const int ld_t = P.wide ? P.ld_m : P.ld_n;
+      ld_t = P.wide ? P.ld_m : P.ld_n;
       void* xa_next = (s.t & 1) ? P.xa0 : P.xa1;
-      T* cs = (T*)(P.wide ? P.xg : xa_next) + (int64_t)slice * rows * ld_s;
-      T* ct = (T*)(P.wide ? xa_next : P.xg) + (int64_t)slice * cols * ld_t;
+      dst = (T*)(P.wide ? P.xg : xa_next) + (int64_t)slice * rows * ld_s;
+      dstT = (T*)(P.wide ? xa_next : P.xg) + (int64_t)slice * cols * ld_t;
+      ld_dst = ld_s;
+      ldst_lim = ld_s;
+      t_rows_lim = cols;
+    }
+  }
+  float acc_sq = 0.f;
+  const int lane = tid & 63, wave = tid >> 6;
+  const int wr = wave >> 2, wc = wave & 3, h = lane >> 5, r32 = lane & 31;
+#pragma unroll 1
+  for (int hf = 0; hf < 2; ++hf) {
+    // (1) the four waves holding rows [128·hf, 128·hf + 128) stage their accumulators
+    if (wr == hf) {
 #pragma unroll
       for (int i = 0; i < 4; ++i)
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const int gc = col0 + acc_col(j);
+        for (int j = 0; j < 2; ++j)
 #pragma unroll
           for (int r = 0; r < 16; ++r) {
-            const int gr = row0 + acc_row(i, r);
-            float xn = 0.f;
-            if (gr < rows && gc < cols) {
-              const int64_t o = (int64_t)gr * cols + gc;
-              xn = fmaf(alpha, xf[o], acc[i][j][r]);
-              xf[o] = xn;
-              acc_sq = fmaf(xn, xn, acc_sq);
-            }
-            const T tv = Op<T>::from(xn);
-            if (gr < rows && gc < ld_s) cs[(int64_t)gr * ld_s + gc] = tv;
-            if (gc < cols && gr < ld_t) ct[(int64_t)gc * ld_t + gr] = tv;
+            const int rr = i * 32 + (r >> 2) * 8 + h * 4 + (r & 3);
+            const int cc = wc * 64 + j * 32 + r32;
+            *(float*)(smem + stage_off(rr, cc)) = acc[i][j][r];
           }
-        }
-      const float tot = block_sum(acc_sq, red);
-      if (threadIdx.x == 0) P.part_apply[(int64_t)slice * P.apply_tr * P.apply_tc + u] = tot;
     }
+    __syncthreads();
+    // (2) row pass: 128 rows × 64 chunks of 4 columns
+#pragma unroll 4
+    for (int k = 0; k < 16; ++k) {
+      const int id = tid + kGemmThreads * k;
+      const int rr = id >> 6, cq = id & 63;
+      float* sp = (float*)(smem + rr * 1024 + ((cq ^ ((rr >> 3) & 15)) << 4));
+      float4 a4 = *(const float4*)sp;
+      float v[4] = {a4.x, a4.y, a4.z, a4.w};
+      const int gr = row0 + hf * 128 + rr, gc = col0 + 4 * cq;
+      const bool rok = gr < rows_lim;
+      if (PH == PH_GRAM) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          if (gr == gc + e && rok) v[e] -= d;
+      } else if (PH == PH_SQUARE) {
+        float ap[4] = {0.f, 0.f, 0.f, 0.f};
+        if (rok && gc < ldm) load4(aprime + (int64_t)gr * ldm + gc, ap);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) v[e] = fmaf(lin, ap[e], s.c * v[e]);
+      } else {
+        float x[4] = {0.f, 0.f, 0.f, 0.f};
+        if (rok && gc < cols) {
+          const float4 x4 = *(const float4*)(xf + (int64_t)gr * P.ld_x + gc);
+          x[0] = x4.x; x[1] = x4.y; x[2] = x4.z; x[3] = x4.w;
+        }
+#pragma unroll
+        for (int e = 0; e < 4; ++e) v[e] = (rok && gc + e < cols) ? fmaf(alpha, x[e], v[e]) : 0.f;
+        if (s.last) {
+          if (rok && gc < cols) {
+            if (vec_user) {
+              const int64_t o = (int64_t)gr * cols + gc;
+              if (outp) *(float4*)(outp + o) = make_float4(v[0], v[1], v[2], v[3]);
+              if (wst) {
+                float4 w4 = *(const float4*)(wst + o);
+                w4.x = fmaf(-s.lr, v[0], s.decay * w4.x);
+                w4.y = fmaf(-s.lr, v[1], s.decay * w4.y);
+                w4.z = fmaf(-s.lr, v[2], s.decay * w4.z);
+                w4.w = fmaf(-s.lr, v[3], s.decay * w4.w);
+                *(float4*)(wst + o) = w4;
+              }
+            } else {
+#pragma unroll
+              for (int e = 0; e < 4; ++e) {
+                if (gc + e >= cols) break;
+                const int64_t o = (int64_t)gr * cols + gc + e;
+                if (outp) outp[o] = v[e];
+                if (wst) wst[o] = fmaf(-s.lr, v[e], s.decay * wst[o]);
+              }
+            }
+          }
+          continue;
+        }
+        if (rok && gc < cols) {
+          *(float4*)(xf + (int64_t)gr * P.ld_x + gc) = make_float4(v[0], v[1], v[2], v[3]);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) acc_sq = fmaf(v[e], v[e], acc_sq);
+        }
+      }
+      if (rok && gc < (PH == PH_APPLY ? ldst_lim : ldm)) store4(dst + (int64_t)gr * ld_dst + gc, v[0], v[1], v[2], v[3]);
+      if (dstT) *(float4*)sp = make_float4(v[0], v[1], v[2], v[3]);
+    }
+    __syncthreads();
+    // (3) column pass: transposed destination rows = tile columns
+    if (dstT) {
+      constexpr int RPC = 16 / (int)sizeof(T);          // rows per 16-byte chunk
+      constexpr int CPC = 128 / RPC;                    // chunks per column (this half)
+#pragma unroll 2
+      for (int k = 0; k < (256 * CPC) / kGemmThreads; ++k) {
+        const int id = tid + kGemmThreads * k;
+        const int cc = id / CPC, rg = id % CPC;
+        const int trow = col0 + cc;                       // row of the transposed destination
+        const int tcol = row0 + hf * 128 + rg * RPC;      // first column written
+        if (trow >= t_rows_lim || tcol >= (PH == PH_APPLY ? ld_t : ldm)) continue;
+        float v[RPC];
+#pragma unroll
+        for (int e = 0; e < RPC; ++e) v[e] = *(const float*)(smem + stage_off(rg * RPC + e, cc));
+        store_row16(dstT + (int64_t)trow * (PH == PH_APPLY ? ld_t : ldm) + tcol, v);
+      }
+    }
+    __syncthreads();
   }
+  if (PH == PH_APPLY && !s.last) {
+    const float tot = block_sum<kGemmWaves>(acc_sq, red);
+    if (threadIdx.x == 0) P.part_apply[(int64_t)slice * P.apply_tr * P.apply_tc + u] = tot;
+  }
+  (void)cols_lim;
 }
 
 // plain C = A·Bᵀ (fp32 out) on the same core: the contraction test hook
@@ -539,28 +718,28 @@ struct GemmArgs {
 };
 
 template <typename T>
-__global__ __launch_bounds__(kThreads, 1) void k_gemm_plain(GemmArgs g) {
+__global__ __launch_bounds__(kGemmThreads) void k_gemm_plain(GemmArgs g) {
   extern __shared__ __align__(16) char smem[];
   const int row0 = (blockIdx.x / g.tiles_n) * kTile;
   const int col0 = (blockIdx.x % g.tiles_n) * kTile;
   Operands op;
   op.a = (const char*)((const T*)g.A + row0 * g.lda);
   op.b = (const char*)((const T*)g.B + col0 * g.ldb);
-  op.lda_b = g.lda * (int64_t)sizeof(T);
-  op.ldb_b = g.ldb * (int64_t)sizeof(T);
+  op.lda_b = (int)(g.lda * (int64_t)sizeof(T));
+  op.ldb_b = (int)(g.ldb * (int64_t)sizeof(T));
   op.rows_a = (int)(g.M - row0);
   op.rows_b = (int)(g.N - col0);
   op.ktiles = g.ktiles;
-  f32x16_t acc[4][4];
+  f32x16_t acc[4][2];
   gemm_mainloop<T>(op, smem, acc);
 #pragma unroll
   for (int i = 0; i < 4; ++i)
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
+    for (int j = 0; j < 2; ++j) {
       const int64_t gc = col0 + acc_col(j);
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const int64_t gr = row0 + acc_row(i, r);
+        const int64_t gr = row0 + acc_row(i, r >> 2) + (r & 3);
         if (gr < g.M && gc < g.N) g.C[gr * g.ldc + gc] = acc[i][j][r];
       }
     }
@@ -598,7 +777,7 @@ static int ensure_lds(int f32) {
 int launch_phase(int phase, int prec_f32, const LaunchTable& tab, const LaunchScalars& s, void* stream) {
   if (tab.total_wg <= 0) return 0;
   hipStream_t st = (hipStream_t)stream;
-  const dim3 grid(tab.total_wg), block(kThreads);
+  const dim3 grid(tab.total_wg), block(kThreads), gblock(kGemmThreads);
   int e = ensure_lds(prec_f32);
   if (e) return e;
   timing_before(phase, stream);
@@ -609,16 +788,16 @@ int launch_phase(int phase, int prec_f32, const LaunchTable& tab, const LaunchSc
       else hipLaunchKernelGGL(k_start<uint16_t>, grid, block, 0, st, tab, s);
       break;
     case PH_GRAM:
-      if (prec_f32) hipLaunchKernelGGL((k_gemm<float, PH_GRAM>), grid, block, kGemmLds, st, tab, s);
-      else hipLaunchKernelGGL((k_gemm<uint16_t, PH_GRAM>), grid, block, kGemmLds, st, tab, s);
+      if (prec_f32) hipLaunchKernelGGL((k_gemm<float, PH_GRAM>), grid, gblock, kGemmLds, st, tab, s);
+      else hipLaunchKernelGGL((k_gemm<uint16_t, PH_GRAM>), grid, gblock, kGemmLds, st, tab, s);
       break;
     case PH_SQUARE:
-      if (prec_f32) hipLaunchKernelGGL((k_gemm<float, PH_SQUARE>), grid, block, kGemmLds, st, tab, s);
-      else hipLaunchKernelGGL((k_gemm<uint16_t, PH_SQUARE>), grid, block, kGemmLds, st, tab, s);
+      if (prec_f32) hipLaunchKernelGGL((k_gemm<float, PH_SQUARE>), grid, gblock, kGemmLds, st, tab, s);
+      else hipLaunchKernelGGL((k_gemm<uint16_t, PH_SQUARE>), grid, gblock, kGemmLds, st, tab, s);
       break;
     case PH_APPLY:
-      if (prec_f32) hipLaunchKernelGGL((k_gemm<float, PH_APPLY>), grid, block, kGemmLds, st, tab, s);
-      else hipLaunchKernelGGL((k_gemm<uint16_t, PH_APPLY>), grid, block, kGemmLds, st, tab, s);
+      if (prec_f32) hipLaunchKernelGGL((k_gemm<float, PH_APPLY>), grid, gblock, kGemmLds, st, tab, s);
+      else hipLaunchKernelGGL((k_gemm<uint16_t, PH_APPLY>), grid, gblock, kGemmLds, st, tab, s);
       break;
     case PH_UPDATE: hipLaunchKernelGGL(k_update, grid, block, 0, st, tab, s); break;
     default: return (int)hipErrorInvalidValue;
@@ -636,9 +815,9 @@ int launch_gemm_nt(const void* A, const void* B, float* C, int64_t M, int64_t N,
   GemmArgs g;
   g.A = A; g.B = B; g.C = C; g.M = M; g.N = N; g.lda = lda; g.ldb = ldb; g.ldc = ldc;
   const int64_t kpad = round_up(K, kLdAlign);
-  g.ktiles = (int)(kpad / (f32 ? 32 : 64));
+  g.ktiles = (int)(kpad * (f32 ? 4 : 2) / kRowBytes);
   g.tiles_n = (int)cdiv(N, kTile);
-  const dim3 grid((unsigned)(cdiv(M, kTile) * g.tiles_n)), block(kThreads);
+  const dim3 grid((unsigned)(cdiv(M, kTile) * g.tiles_n)), block(kGemmThreads);
   hipStream_t st = (hipStream_t)stream;
   timing_before(PH_GEMM, stream);
   if (f32) hipLaunchKernelGGL(k_gemm_plain<float>, grid, block, kGemmLds, st, g);
