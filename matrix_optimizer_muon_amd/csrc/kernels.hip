@@ -323,7 +323,8 @@ __device__ __forceinline__ void mfma_chunk<float>(f32x16_t& acc, const u32x4_t& 
 
 template <typename T>
 __device__ __forceinline__ void gemm_mainloop(const Operands& op, char* smem, f32x16_t (&acc)[4][2]) {
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);    // wave-uniform
   const int wr = wave >> 2, wc = wave & 3, h = lane >> 5, r32 = lane & 31;
   const __amdgpu_buffer_rsrc_t ra = __builtin_amdgcn_make_buffer_rsrc(
       (void*)op.a, 0, (op.rows_a < kTile ? op.rows_a : kTile) * op.lda_b, 0x00020000);
@@ -388,32 +389,37 @@ __device__ __forceinline__ void gemm_mainloop(const Operands& op, char* smem, f3
 #pragma unroll
       for (int j = 0; j < 2; ++j) mfma_chunk<T>(acc[i][j], fa[buf][i], fb[buf][j]);
   };
-
-  const int KT = op.ktiles;
-#pragma unroll
-  for (int s = 0; s < kStages - 1; ++s)
-    if (s < KT) issue(s);
-  if (kStages - 2 < KT) DMUON_WAIT_VM(kDmaPerStage * (kStages - 2));
-  else DMUON_WAIT_VM(0);
-  __builtin_amdgcn_s_barrier();
-  fload(0, 0, 0);
-  for (int kt = 0; kt < KT; ++kt) {
+  // mode 0: steady state (issue stage kt + 3, wait for stage kt + 1 with one younger
+  // stage in flight); 1: tail (nothing left to issue, wait for everything); 2: last stage
+  auto body = [&](int kt, int mode) {
     fload(kt, 1, 1);
     __builtin_amdgcn_sched_barrier(0);
     mmas(0);
     __builtin_amdgcn_sched_barrier(0);
-    if (kt + 1 < KT) {
-      // stage kt+1 landed for every wave, and every wave is done reading stage kt-1
-      if (kt + kStages - 2 < KT) DMUON_WAIT_VM(kDmaPerStage * (kStages - 3));
+    if (mode != 2) {
+      if (mode == 0) DMUON_WAIT_VM(kDmaPerStage * (kStages - 3));
       else DMUON_WAIT_VM(0);
+      // stage kt+1 landed for every wave, and every wave is done reading stage kt-1
       __builtin_amdgcn_s_barrier();
-      if (kt + kStages - 1 < KT) issue(kt + kStages - 1);
+      if (mode == 0) issue(kt + kStages - 1);
       fload(kt + 1, 0, 0);
     }
     __builtin_amdgcn_sched_barrier(0);
     mmas(1);
     __builtin_amdgcn_sched_barrier(0);
-  }
+  };
+
+  const int KT = op.ktiles;   // ≥ 2 (leading dims are multiples of 64 elements)
+  const int pro = KT < kStages - 1 ? KT : kStages - 1;
+  for (int st = 0; st < pro; ++st) issue(st);
+  if (KT >= kStages - 1) DMUON_WAIT_VM(kDmaPerStage * (kStages - 2));
+  else DMUON_WAIT_VM(0);
+  __builtin_amdgcn_s_barrier();
+  fload(0, 0, 0);
+  int kt = 0;
+  for (; kt + kStages - 1 < KT; ++kt) body(kt, 0);
+  for (; kt + 1 < KT; ++kt) body(kt, 1);
+  body(kt, 2);
   // all LDS reads done before the caller reuses LDS
   __syncthreads();
 }
@@ -486,7 +492,7 @@ __device__ __forceinline__ int xcd_logical_block() {
   return (xcd < rem ? xcd * (per + 1) : rem * (per + 1) + (xcd - rem) * per) + local;
 }
 
-template <typename T, int PH>
+template <typename T, int PH, bool LAST>
 __global__ __launch_bounds__(kGemmThreads) void k_gemm(LaunchTable tab, LaunchScalars s) {
   extern __shared__ __align__(16) char smem[];
   __shared__ float red[kGemmWaves];
@@ -583,7 +589,7 @@ __global__ __launch_bounds__(kGemmThreads) void k_gemm(LaunchTable tab, LaunchSc
     xf = P.xf + (int64_t)slice * rows * P.ld_x;
     rows_lim = rows;
     cols_lim = cols;
-    if (s.last) {
+    if (LAST) {
       const int64_t per = (int64_t)rows * cols;
       wst = s.write_master ? P.master + (int64_t)slice * per : nullptr;
       outp = P.out ? P.out + (int64_t)slice * per : nullptr;
@@ -619,66 +625,96 @@ __global__ __launch_bounds__(kGemmThreads) void k_gemm(LaunchTable tab, LaunchSc
           }
     }
     __syncthreads();
-    // (2) row pass: 128 rows × 64 chunks of 4 columns
-#pragma unroll 4
-    for (int k = 0; k < 16; ++k) {
-      const int id = tid + kGemmThreads * k;
-      const int rr = id >> 6, cq = id & 63;
-      float* sp = (float*)(smem + rr * 1024 + ((cq ^ ((rr >> 3) & 15)) << 4));
-      float4 a4 = *(const float4*)sp;
-      float v[4] = {a4.x, a4.y, a4.z, a4.w};
-      const int gr = row0 + hf * 128 + rr, gc = col0 + 4 * cq;
-      const bool rok = gr < rows_lim;
-      if (PH == PH_GRAM) {
+    // (2) row pass: 128 rows × 64 chunks of 4 columns, in two batches of 8 chunks
+    // per thread; each batch issues all its global loads before any store, since
+    // loads and stores share one in-order completion counter.
+#pragma unroll 1
+    for (int kb = 0; kb < 16; kb += 8) {
+      float4 xin[8], win[LAST ? 8 : 1];
+      uint2 ain[8];
 #pragma unroll
-        for (int e = 0; e < 4; ++e)
-          if (gr == gc + e && rok) v[e] -= d;
-      } else if (PH == PH_SQUARE) {
-        float ap[4] = {0.f, 0.f, 0.f, 0.f};
-        if (rok && gc < ldm) load4(aprime + (int64_t)gr * ldm + gc, ap);
-#pragma unroll
-        for (int e = 0; e < 4; ++e) v[e] = fmaf(lin, ap[e], s.c * v[e]);
-      } else {
-        float x[4] = {0.f, 0.f, 0.f, 0.f};
-        if (rok && gc < cols) {
-          const float4 x4 = *(const float4*)(xf + (int64_t)gr * P.ld_x + gc);
-          x[0] = x4.x; x[1] = x4.y; x[2] = x4.z; x[3] = x4.w;
-        }
-#pragma unroll
-        for (int e = 0; e < 4; ++e) v[e] = (rok && gc + e < cols) ? fmaf(alpha, x[e], v[e]) : 0.f;
-        if (s.last) {
-          if (rok && gc < cols) {
-            if (vec_user) {
-              const int64_t o = (int64_t)gr * cols + gc;
-              if (outp) *(float4*)(outp + o) = make_float4(v[0], v[1], v[2], v[3]);
-              if (wst) {
-                float4 w4 = *(const float4*)(wst + o);
-                w4.x = fmaf(-s.lr, v[0], s.decay * w4.x);
-                w4.y = fmaf(-s.lr, v[1], s.decay * w4.y);
-                w4.z = fmaf(-s.lr, v[2], s.decay * w4.z);
-                w4.w = fmaf(-s.lr, v[3], s.decay * w4.w);
-                *(float4*)(wst + o) = w4;
-              }
-            } else {
-#pragma unroll
-              for (int e = 0; e < 4; ++e) {
-                if (gc + e >= cols) break;
-                const int64_t o = (int64_t)gr * cols + gc + e;
-                if (outp) outp[o] = v[e];
-                if (wst) wst[o] = fmaf(-s.lr, v[e], s.decay * wst[o]);
-              }
-            }
+      for (int q = 0; q < 8; ++q) {
+        const int id = tid + kGemmThreads * (kb + q);
+        const int rr = id >> 6, cq = id & 63;
+        const int gr = row0 + hf * 128 + rr, gc = col0 + 4 * cq;
+        const bool rok = gr < rows_lim;
+        xin[q] = make_float4(0.f, 0.f, 0.f, 0.f);
+        if (LAST) win[LAST ? q : 0] = make_float4(0.f, 0.f, 0.f, 0.f);
+        ain[q] = make_uint2(0u, 0u);
+        if (PH == PH_SQUARE) {
+          if (rok && gc < ldm) {
+            if (sizeof(T) == 2) ain[q] = *(const uint2*)(aprime + (int64_t)gr * ldm + gc);
+            else xin[q] = *(const float4*)(aprime + (int64_t)gr * ldm + gc);
           }
-          continue;
-        }
-        if (rok && gc < cols) {
-          *(float4*)(xf + (int64_t)gr * P.ld_x + gc) = make_float4(v[0], v[1], v[2], v[3]);
-#pragma unroll
-          for (int e = 0; e < 4; ++e) acc_sq = fmaf(v[e], v[e], acc_sq);
+        } else if (PH == PH_APPLY) {
+          if (rok && gc < cols) {
+            xin[q] = *(const float4*)(xf + (int64_t)gr * P.ld_x + gc);
+            if (LAST && wst && vec_user) win[LAST ? q : 0] = *(const float4*)(wst + (int64_t)gr * cols + gc);
+          }
         }
       }
-      if (rok && gc < (PH == PH_APPLY ? ldst_lim : ldm)) store4(dst + (int64_t)gr * ld_dst + gc, v[0], v[1], v[2], v[3]);
-      if (dstT) *(float4*)sp = make_float4(v[0], v[1], v[2], v[3]);
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int q = 0; q < 8; ++q) {
+        const int id = tid + kGemmThreads * (kb + q);
+        const int rr = id >> 6, cq = id & 63;
+        float* sp = (float*)(smem + rr * 1024 + ((cq ^ ((rr >> 3) & 15)) << 4));
+        const float4 a4 = *(const float4*)sp;
+        float v[4] = {a4.x, a4.y, a4.z, a4.w};
+        const int gr = row0 + hf * 128 + rr, gc = col0 + 4 * cq;
+        const bool rok = gr < rows_lim;
+        if (PH == PH_GRAM) {
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            if (gr == gc + e && rok) v[e] -= d;
+        } else if (PH == PH_SQUARE) {
+          float ap[4];
+          if (sizeof(T) == 2) {
+            ap[0] = __uint_as_float(ain[q].x << 16); ap[1] = __uint_as_float(ain[q].x & 0xffff0000u);
+            ap[2] = __uint_as_float(ain[q].y << 16); ap[3] = __uint_as_float(ain[q].y & 0xffff0000u);
+          } else {
+            ap[0] = xin[q].x; ap[1] = xin[q].y; ap[2] = xin[q].z; ap[3] = xin[q].w;
+          }
+#pragma unroll
+          for (int e = 0; e < 4; ++e) v[e] = fmaf(lin, ap[e], s.c * v[e]);
+        } else {
+          const float x[4] = {xin[q].x, xin[q].y, xin[q].z, xin[q].w};
+#pragma unroll
+          for (int e = 0; e < 4; ++e) v[e] = (rok && gc + e < cols) ? fmaf(alpha, x[e], v[e]) : 0.f;
+          if (LAST) {
+            if (rok && gc < cols) {
+              if (vec_user) {
+                const int64_t o = (int64_t)gr * cols + gc;
+                if (outp) *(float4*)(outp + o) = make_float4(v[0], v[1], v[2], v[3]);
+                if (wst) {
+                  float4 w4 = win[LAST ? q : 0];
+                  w4.x = fmaf(-s.lr, v[0], s.decay * w4.x);
+                  w4.y = fmaf(-s.lr, v[1], s.decay * w4.y);
+                  w4.z = fmaf(-s.lr, v[2], s.decay * w4.z);
+                  w4.w = fmaf(-s.lr, v[3], s.decay * w4.w);
+                  *(float4*)(wst + o) = w4;
+                }
+              } else {
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                  if (gc + e >= cols) break;
+                  const int64_t o = (int64_t)gr * cols + gc + e;
+                  if (outp) outp[o] = v[e];
+                  if (wst) wst[o] = fmaf(-s.lr, v[e], s.decay * wst[o]);
+                }
+              }
+            }
+            continue;
+          }
+          if (rok && gc < cols) {
+            *(float4*)(xf + (int64_t)gr * P.ld_x + gc) = make_float4(v[0], v[1], v[2], v[3]);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) acc_sq = fmaf(v[e], v[e], acc_sq);
+          }
+        }
+        if (rok && gc < (PH == PH_APPLY ? ldst_lim : ldm)) store4(dst + (int64_t)gr * ld_dst + gc, v[0], v[1], v[2], v[3]);
+        if (dstT) *(float4*)sp = make_float4(v[0], v[1], v[2], v[3]);
+      }
     }
     __syncthreads();
     // (3) column pass: transposed destination rows = tile columns
@@ -700,7 +736,7 @@ __global__ __launch_bounds__(kGemmThreads) void k_gemm(LaunchTable tab, LaunchSc
     }
     __syncthreads();
   }
-  if (PH == PH_APPLY && !s.last) {
+  if (PH == PH_APPLY && !LAST) {
     const float tot = block_sum<kGemmWaves>(acc_sq, red);
     if (threadIdx.x == 0) P.part_apply[(int64_t)slice * P.apply_tr * P.apply_tc + u] = tot;
   }
@@ -760,14 +796,16 @@ static int ensure_lds(int f32) {
   if (flag) return 0;
   int e = 0;
   if (f32) {
-    e |= set_lds(k_gemm<float, PH_GRAM>);
-    e |= set_lds(k_gemm<float, PH_SQUARE>);
-    e |= set_lds(k_gemm<float, PH_APPLY>);
+    e |= set_lds(k_gemm<float, PH_GRAM, false>);
+    e |= set_lds(k_gemm<float, PH_SQUARE, false>);
+    e |= set_lds(k_gemm<float, PH_APPLY, false>);
+    e |= set_lds(k_gemm<float, PH_APPLY, true>);
     e |= set_lds(k_gemm_plain<float>);
   } else {
-    e |= set_lds(k_gemm<uint16_t, PH_GRAM>);
-    e |= set_lds(k_gemm<uint16_t, PH_SQUARE>);
-    e |= set_lds(k_gemm<uint16_t, PH_APPLY>);
+    e |= set_lds(k_gemm<uint16_t, PH_GRAM, false>);
+    e |= set_lds(k_gemm<uint16_t, PH_SQUARE, false>);
+    e |= set_lds(k_gemm<uint16_t, PH_APPLY, false>);
+    e |= set_lds(k_gemm<uint16_t, PH_APPLY, true>);
     e |= set_lds(k_gemm_plain<uint16_t>);
   }
   if (e == 0) flag = 1;
@@ -788,16 +826,16 @@ int launch_phase(int phase, int prec_f32, const LaunchTable& tab, const LaunchSc
       else hipLaunchKernelGGL(k_start<uint16_t>, grid, block, 0, st, tab, s);
       break;
     case PH_GRAM:
-      if (prec_f32) hipLaunchKernelGGL((k_gemm<float, PH_GRAM>), grid, gblock, kGemmLds, st, tab, s);
-      else hipLaunchKernelGGL((k_gemm<uint16_t, PH_GRAM>), grid, gblock, kGemmLds, st, tab, s);
+      if (prec_f32) hipLaunchKernelGGL((k_gemm<float, PH_GRAM, false>), grid, gblock, kGemmLds, st, tab, s);
+      else hipLaunchKernelGGL((k_gemm<uint16_t, PH_GRAM, false>), grid, gblock, kGemmLds, st, tab, s);
       break;
     case PH_SQUARE:
-      if (prec_f32) hipLaunchKernelGGL((k_gemm<float, PH_SQUARE>), grid, gblock, kGemmLds, st, tab, s);
-      else hipLaunchKernelGGL((k_gemm<uint16_t, PH_SQUARE>), grid, gblock, kGemmLds, st, tab, s);
+      if (prec_f32) hipLaunchKernelGGL((k_gemm<float, PH_SQUARE, false>), grid, gblock, kGemmLds, st, tab, s);
+      else hipLaunchKernelGGL((k_gemm<uint16_t, PH_SQUARE, false>), grid, gblock, kGemmLds, st, tab, s);
       break;
     case PH_APPLY:
-      if (prec_f32) hipLaunchKernelGGL((k_gemm<float, PH_APPLY>), grid, gblock, kGemmLds, st, tab, s);
-      else hipLaunchKernelGGL((k_gemm<uint16_t, PH_APPLY>), grid, gblock, kGemmLds, st, tab, s);
+      if (prec_f32) { if (s.last) hipLaunchKernelGGL((k_gemm<float, PH_APPLY, true>), grid, gblock, kGemmLds, st, tab, s); else hipLaunchKernelGGL((k_gemm<float, PH_APPLY, false>), grid, gblock, kGemmLds, st, tab, s); }
+      else { if (s.last) hipLaunchKernelGGL((k_gemm<uint16_t, PH_APPLY, true>), grid, gblock, kGemmLds, st, tab, s); else hipLaunchKernelGGL((k_gemm<uint16_t, PH_APPLY, false>), grid, gblock, kGemmLds, st, tab, s); }
       break;
     case PH_UPDATE: hipLaunchKernelGGL(k_update, grid, block, 0, st, tab, s); break;
     default: return (int)hipErrorInvalidValue;
