@@ -156,7 +156,7 @@ static int build_plan(const std::vector<Item>& items, int prec_f32, Plan& pl, ch
     P.part_apply = (float*)carve((size_t)(b * P.apply_tr * P.apply_tc) * 4);
     const int64_t tri = (int64_t)P.tiles_m * (P.tiles_m + 1) / 2;
     const int64_t cnt[PH_COUNT] = {b * P.chunks, b * P.prep_tiles_r * P.prep_tiles_c, b * tri, b * tri,
-                                   b * P.apply_tr * P.apply_tc, b * P.chunks, 0};
+                                   b * P.apply_tr * P.apply_tc, b * P.chunks, 0, b};
     for (int ph = 0; ph < PH_COUNT; ++ph) {
       P.wg0[ph] = (int32_t)wg[ph];
       pl.prefix[(size_t)ph * (n + 1) + i] = (int32_t)wg[ph];
@@ -194,6 +194,7 @@ static int run_plan(Plan& pl, char* ws, int prec_f32, const LaunchScalars& base_
   s.t = 0;
   s.last = 0;
   if ((e = go(PH_MOMENTUM, s))) return e;
+  if ((e = go(PH_NORM, s))) return e;
   if ((e = go(PH_START, s))) return e;
   if (steps == 0) return go(PH_UPDATE, s);
   for (int t = 0; t < steps; ++t) {

@@ -25,7 +25,8 @@ enum Phase : int {
   PH_APPLY = 4,      // X ← (a + bd + cd²) X + B' X (last: decay + update)
   PH_UPDATE = 5,     // W ← (1 − lr wd) W − lr X0 (only when k = 0)
   PH_GEMM = 6,       // test hook: plain NT product
-  PH_COUNT = 7
+  PH_NORM = 7,       // per-slice norm finalize: inv = 1/(‖B‖_F + eps), d₀
+  PH_COUNT = 8
 };
 
 // One tensor (2-D = batch 1, or 3-D batch of slices) as the kernels see it.

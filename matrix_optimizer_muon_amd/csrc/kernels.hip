@@ -161,15 +161,75 @@ __global__ __launch_bounds__(kThreads) void k_momentum(LaunchTable tab, LaunchSc
   if (threadIdx.x == 0) P.part_norm[(int64_t)slice * P.chunks + chunk] = tot;
 }
 
+// Store 4 consecutive elements (rows gr0..gr0+3 of the tile, one column) as one
+// vector into a transposed row: dst[col][gr0 .. gr0+3].
+__device__ __forceinline__ void store4(uint16_t* p, float a, float b, float c, float d) {
+  const uint32_t lo = (uint32_t)f32_to_bf16(a) | ((uint32_t)f32_to_bf16(b) << 16);
+  const uint32_t hi = (uint32_t)f32_to_bf16(c) | ((uint32_t)f32_to_bf16(d) << 16);
+  *(uint2*)p = make_uint2(lo, hi);
+}
+__device__ __forceinline__ void store4(float* p, float a, float b, float c, float d) {
+  *(float4*)p = make_float4(a, b, c, d);
+}
+
+// Byte offset of element (r, c) of a staged 128×256 fp32 half-tile: 1 KiB rows,
+// 16-byte chunks XOR-swizzled by (r >> 3) & 15 so that row-contiguous 16-byte
+// reads and reads of one column over 16 row groups both spread over all banks.
+__device__ __forceinline__ int stage_off(int r, int c) {
+  return r * 1024 + ((((c >> 2) ^ ((r >> 3) & 15)) << 4) | ((c & 3) << 2));
+}
+
+__device__ __forceinline__ void load4(const uint16_t* p, float (&v)[4]) {
+  const uint2 u = *(const uint2*)p;
+  v[0] = __uint_as_float(u.x << 16); v[1] = __uint_as_float(u.x & 0xffff0000u);
+  v[2] = __uint_as_float(u.y << 16); v[3] = __uint_as_float(u.y & 0xffff0000u);
+}
+__device__ __forceinline__ void load4(const float* p, float (&v)[4]) {
+  const float4 u = *(const float4*)p;
+  v[0] = u.x; v[1] = u.y; v[2] = u.z; v[3] = u.w;
+}
+
+// 16 bytes of one destination row: 8 bf16 or 4 fp32 values
+__device__ __forceinline__ void store_row16(uint16_t* p, const float (&v)[8]) {
+  uint4 u;
+  u.x = (uint32_t)f32_to_bf16(v[0]) | ((uint32_t)f32_to_bf16(v[1]) << 16);
+  u.y = (uint32_t)f32_to_bf16(v[2]) | ((uint32_t)f32_to_bf16(v[3]) << 16);
+  u.z = (uint32_t)f32_to_bf16(v[4]) | ((uint32_t)f32_to_bf16(v[5]) << 16);
+  u.w = (uint32_t)f32_to_bf16(v[6]) | ((uint32_t)f32_to_bf16(v[7]) << 16);
+  *(uint4*)p = u;
+}
+__device__ __forceinline__ void store_row16(float* p, const float (&v)[4]) {
+  *(float4*)p = make_float4(v[0], v[1], v[2], v[3]);
+}
+
 // ---------------------------------------------------------------------------
-// start: X₀ = inv·B (inv = 1/(‖B‖_F + eps), or 1 without normalisation);
-// fp32 iterate in storage layout, operand copy in storage layout, operand copy
-// transposed (through LDS), zero padding up to the 64-element leading dims.
+// norm finalize: one workgroup per slice sums the momentum kernel's partials in
+// a fixed order: inv = 1/(‖B‖_F + eps) (1 without normalisation), d₀ = ‖X₀‖²_F/m
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(kThreads) void k_norm(LaunchTable tab, LaunchScalars s) {
+  __shared__ float red[4];
+  const int bid = blockIdx.x;
+  const int p = find_prob(tab.wg_prefix + PH_NORM * (tab.n_probs + 1), tab.n_probs, bid);
+  const DevProblem& P = tab.probs[p];
+  const int slice = bid - P.wg0[PH_NORM];
+  const float total = sum_partials<4>(P.part_norm + (int64_t)slice * P.chunks, P.chunks, red);
+  if (threadIdx.x == 0) {
+    const float inv = s.normalize ? 1.0f / (sqrtf(total) + s.eps) : 1.0f;
+    float* scal = tab.scal + (int64_t)(P.slice_base + slice) * kScalStride;
+    scal[0] = inv;
+    scal[1] = total * inv * inv / (float)P.m;   // d₀ = ‖X₀‖²_F / m
+  }
+}
+
+// ---------------------------------------------------------------------------
+// start: X₀ = inv·B into the fp32 iterate (storage layout), the operand copy in
+// storage layout, and the transposed operand copy through a 64×64 LDS tile; zero
+// padding up to the 64-element leading dims.  All global accesses are 16-byte
+// (or 8-byte for a bf16 copy) row vectors when the row length allows.
 // ---------------------------------------------------------------------------
 template <typename T>
 __global__ __launch_bounds__(kThreads) void k_start(LaunchTable tab, LaunchScalars s) {
   __shared__ float tile[kPrepTile][kPrepTile + 1];
-  __shared__ float red[4];
   const int bid = blockIdx.x;
   const int p = find_prob(tab.wg_prefix + PH_START * (tab.n_probs + 1), tab.n_probs, bid);
   const DevProblem& P = tab.probs[p];
@@ -178,14 +238,7 @@ __global__ __launch_bounds__(kThreads) void k_start(LaunchTable tab, LaunchScala
   const int slice = local / per_slice, tt = local % per_slice;
   const int r0 = (tt / P.prep_tiles_c) * kPrepTile, c0 = (tt % P.prep_tiles_c) * kPrepTile;
   const int rows = P.rows, cols = P.cols;
-
-  const float total = sum_partials<4>(P.part_norm + (int64_t)slice * P.chunks, P.chunks, red);
-  const float inv = s.normalize ? 1.0f / (sqrtf(total) + s.eps) : 1.0f;
-  float* scal = tab.scal + (int64_t)(P.slice_base + slice) * kScalStride;
-  if (tt == 0 && threadIdx.x == 0) {
-    scal[0] = inv;
-    scal[1] = total * inv * inv / (float)P.m;   // d₀ = ‖X₀‖²_F / m
-  }
+  const float inv = tab.scal[(int64_t)(P.slice_base + slice) * kScalStride];
 
   const int64_t per = (int64_t)rows * cols;
   const float* srcf = s.has_momentum ? P.mom + (int64_t)slice * per
@@ -197,6 +250,10 @@ __global__ __launch_bounds__(kThreads) void k_start(LaunchTable tab, LaunchScala
   const int ld_t = P.wide ? P.ld_m : P.ld_n;    // transposed copy: rows padded
   T* cs = (T*)(P.wide ? P.xg : P.xa0) + (int64_t)slice * rows * ld_s;
   T* ct = (T*)(P.wide ? P.xa0 : P.xg) + (int64_t)slice * cols * ld_t;
+  // rows of 4-element vectors are aligned when cols is a multiple of 4 (and the
+  // source pointer is 16-byte aligned; bf16 sources need 8 bytes)
+  const bool vec = (cols & 3) == 0 &&
+                   (srcb ? (((uintptr_t)srcb & 7) == 0) : (((uintptr_t)srcf & 15) == 0));
 
   const int tr = threadIdx.x >> 4;          // 0..15
   const int tc = (threadIdx.x & 15) * 4;    // 0..60
@@ -204,38 +261,48 @@ __global__ __launch_bounds__(kThreads) void k_start(LaunchTable tab, LaunchScala
   for (int q = 0; q < 4; ++q) {
     const int lr = q * 16 + tr;
     const int r = r0 + lr;
-    float v[4];
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const int c = c0 + tc + e;
-      float x = 0.f;
-      if (r < rows && c < cols) {
-        const int64_t o = (int64_t)r * cols + c;
-        x = (srcb ? bf16_to_f32(srcb[o]) : srcf[o]) * inv;
-        xf[(int64_t)r * P.ld_x + c] = x;
-      }
-      v[e] = x;
-      tile[lr][tc + e] = x;
-    }
+    const int c = c0 + tc;
+    float v[4] = {0.f, 0.f, 0.f, 0.f};
     if (r < rows) {
+      const int64_t o = (int64_t)r * cols + c;
+      if (vec && c + 3 < cols) {
+        if (srcb) {
+          const uint2 u = *(const uint2*)(srcb + o);
+          v[0] = __uint_as_float(u.x << 16); v[1] = __uint_as_float(u.x & 0xffff0000u);
+          v[2] = __uint_as_float(u.y << 16); v[3] = __uint_as_float(u.y & 0xffff0000u);
+        } else {
+          const float4 u = *(const float4*)(srcf + o);
+          v[0] = u.x; v[1] = u.y; v[2] = u.z; v[3] = u.w;
+        }
+      } else {
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int c = c0 + tc + e;
-        if (c < ld_s) cs[(int64_t)r * ld_s + c] = Op<T>::from(v[e]);
+        for (int e = 0; e < 4; ++e)
+          if (c + e < cols) v[e] = srcb ? bf16_to_f32(srcb[o + e]) : srcf[o + e];
       }
+#pragma unroll
+      for (int e = 0; e < 4; ++e) v[e] *= inv;
+      if (c < cols) *(float4*)(xf + (int64_t)r * P.ld_x + c) = make_float4(v[0], v[1], v[2], v[3]);
+      if (c < ld_s) store4(cs + (int64_t)r * ld_s + c, v[0], v[1], v[2], v[3]);
     }
+#pragma unroll
+    for (int e = 0; e < 4; ++e) tile[lr][tc + e] = v[e];
   }
   __syncthreads();
+  // transposed copy: 64 storage columns × 64 storage rows = 8 chunks of 8 rows
+  // (bf16) or 16 chunks of 4 rows (fp32) per column
+  constexpr int RPC = 16 / (int)sizeof(T);
+  constexpr int CPC = kPrepTile / RPC;
 #pragma unroll
-  for (int q = 0; q < 4; ++q) {
-    const int lc = q * 16 + tr;            // storage column = transposed row
-    const int c = c0 + lc;
-    if (c >= cols) continue;
+  for (int k = 0; k < (kPrepTile * CPC) / kThreads; ++k) {
+    const int id = threadIdx.x + kThreads * k;
+    const int lc = id / CPC, rg = id % CPC;
+    const int c = c0 + lc;                  // storage column = transposed row
+    const int r = r0 + rg * RPC;            // first storage row = transposed column
+    if (c >= cols || r >= ld_t) continue;
+    float v[RPC];
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const int r = r0 + tc + e;           // storage row = transposed column
-      if (r < ld_t) ct[(int64_t)c * ld_t + r] = Op<T>::from(tile[tc + e][lc]);
-    }
+    for (int e = 0; e < RPC; ++e) v[e] = tile[rg * RPC + e][lc];
+    store_row16(ct + (int64_t)c * ld_t + r, v);
   }
 }
 
@@ -432,47 +499,6 @@ __device__ __forceinline__ int acc_row(int i, int rq) {   // rq = r >> 2; rows r
 __device__ __forceinline__ int acc_col(int j) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   return (wave & 3) * 64 + j * 32 + (lane & 31);
-}
-
-// Store 4 consecutive elements (rows gr0..gr0+3 of the tile, one column) as one
-// vector into a transposed row: dst[col][gr0 .. gr0+3].
-__device__ __forceinline__ void store4(uint16_t* p, float a, float b, float c, float d) {
-  const uint32_t lo = (uint32_t)f32_to_bf16(a) | ((uint32_t)f32_to_bf16(b) << 16);
-  const uint32_t hi = (uint32_t)f32_to_bf16(c) | ((uint32_t)f32_to_bf16(d) << 16);
-  *(uint2*)p = make_uint2(lo, hi);
-}
-__device__ __forceinline__ void store4(float* p, float a, float b, float c, float d) {
-  *(float4*)p = make_float4(a, b, c, d);
-}
-
-// Byte offset of element (r, c) of a staged 128×256 fp32 half-tile: 1 KiB rows,
-// 16-byte chunks XOR-swizzled by (r >> 3) & 15 so that row-contiguous 16-byte
-// reads and reads of one column over 16 row groups both spread over all banks.
-__device__ __forceinline__ int stage_off(int r, int c) {
-  return r * 1024 + ((((c >> 2) ^ ((r >> 3) & 15)) << 4) | ((c & 3) << 2));
-}
-
-__device__ __forceinline__ void load4(const uint16_t* p, float (&v)[4]) {
-  const uint2 u = *(const uint2*)p;
-  v[0] = __uint_as_float(u.x << 16); v[1] = __uint_as_float(u.x & 0xffff0000u);
-  v[2] = __uint_as_float(u.y << 16); v[3] = __uint_as_float(u.y & 0xffff0000u);
-}
-__device__ __forceinline__ void load4(const float* p, float (&v)[4]) {
-  const float4 u = *(const float4*)p;
-  v[0] = u.x; v[1] = u.y; v[2] = u.z; v[3] = u.w;
-}
-
-// 16 bytes of one destination row: 8 bf16 or 4 fp32 values
-__device__ __forceinline__ void store_row16(uint16_t* p, const float (&v)[8]) {
-  uint4 u;
-  u.x = (uint32_t)f32_to_bf16(v[0]) | ((uint32_t)f32_to_bf16(v[1]) << 16);
-  u.y = (uint32_t)f32_to_bf16(v[2]) | ((uint32_t)f32_to_bf16(v[3]) << 16);
-  u.z = (uint32_t)f32_to_bf16(v[4]) | ((uint32_t)f32_to_bf16(v[5]) << 16);
-  u.w = (uint32_t)f32_to_bf16(v[6]) | ((uint32_t)f32_to_bf16(v[7]) << 16);
-  *(uint4*)p = u;
-}
-__device__ __forceinline__ void store_row16(float* p, const float (&v)[4]) {
-  *(float4*)p = make_float4(v[0], v[1], v[2], v[3]);
 }
 
 // upper-triangle tile u (row-major over ti ≤ tj) of a T×T tile grid
@@ -838,6 +864,7 @@ int launch_phase(int phase, int prec_f32, const LaunchTable& tab, const LaunchSc
       else { if (s.last) hipLaunchKernelGGL((k_gemm<uint16_t, PH_APPLY, true>), grid, gblock, kGemmLds, st, tab, s); else hipLaunchKernelGGL((k_gemm<uint16_t, PH_APPLY, false>), grid, gblock, kGemmLds, st, tab, s); }
       break;
     case PH_UPDATE: hipLaunchKernelGGL(k_update, grid, block, 0, st, tab, s); break;
+    case PH_NORM: hipLaunchKernelGGL(k_norm, grid, block, 0, st, tab, s); break;
     default: return (int)hipErrorInvalidValue;
   }
   e = (int)hipGetLastError();
