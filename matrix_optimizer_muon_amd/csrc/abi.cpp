@@ -119,8 +119,18 @@ static int build_plan(const std::vector<Item>& items, int prec_f32, Plan& pl, ch
     off = align256(off + bytes);
     return p;
   };
+  // Problems in order of falling contraction length (n, then m; stable), so
+  // every phase's grid starts with its longest tiles and the short ones fill in
+  // behind them.
+  std::vector<int> order(n);
+  for (int i = 0; i < n; ++i) order[i] = i;
+  std::stable_sort(order.begin(), order.end(), [&](int x, int y) {
+    const int64_t nx = std::max(items[x].rows, items[x].cols), ny = std::max(items[y].rows, items[y].cols);
+    if (nx != ny) return nx > ny;
+    return std::min(items[x].rows, items[x].cols) > std::min(items[y].rows, items[y].cols);
+  });
   for (int i = 0; i < n; ++i) {
-    const Item& it = items[i];
+    const Item& it = items[order[i]];
     DevProblem& P = pl.probs[i];
     P.batch = (int32_t)it.batch;
     P.rows = (int32_t)it.rows;

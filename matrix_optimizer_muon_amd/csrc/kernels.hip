@@ -509,13 +509,21 @@ __device__ __forceinline__ void tri_tile(int u, int T, int& ti, int& tj) {
   tj = i + (u - start);
 }
 
-// Logical workgroup index: workgroups are handed to the 8 XCDs round-robin, so
-// give each XCD one contiguous range of logical tiles (they share operand panels
-// in that XCD's L2).
+// Logical workgroup index.  Workgroups are handed to the 8 XCDs round-robin in
+// launch order, so workgroup b runs on XCD b % 8 as its (b / 8)-th workgroup.
+// The logical tile list is consumed in windows of 8·kXcdRun tiles: inside a
+// window each XCD takes kXcdRun consecutive tiles (neighbours share operand
+// panels in that XCD's L2), and all XCDs advance through the list together, so
+// tiles of unequal cost (long-K problems first) are spread over every XCD.  A
+// last partial window keeps the identity map; the map is a bijection on [0, G).
+constexpr int kXcdRun = 32;
 __device__ __forceinline__ int xcd_logical_block() {
   const int G = gridDim.x, b = blockIdx.x;
-  const int xcd = b & 7, local = b >> 3, per = G >> 3, rem = G & 7;
-  return (xcd < rem ? xcd * (per + 1) : rem * (per + 1) + (xcd - rem) * per) + local;
+  constexpr int win = 8 * kXcdRun;
+  const int w = b / win;
+  if ((w + 1) * win > G) return b;
+  const int xcd = b & 7, slot = (b >> 3) - w * kXcdRun;
+  return w * win + xcd * kXcdRun + slot;
 }
 
 template <typename T, int PH, bool LAST>
