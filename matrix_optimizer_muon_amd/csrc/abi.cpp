@@ -149,7 +149,7 @@ static int build_plan(const std::vector<Item>& items, int prec_f32, Plan& pl, ch
     P.apply_tr = (int32_t)cdiv(it.rows, kTile);
     P.apply_tc = (int32_t)cdiv(it.cols, kTile);
     P.slice_base = (int32_t)slice_base;
-    P.ld_x = (int32_t)round_up(it.cols, 4);
+    P.ld_x = (int32_t)round_up(it.cols, 32);   // 128-byte rows
     slice_base += it.batch;
     P.grad = it.grad;
     P.mom = it.mom;

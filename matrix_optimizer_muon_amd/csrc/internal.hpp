@@ -44,7 +44,7 @@ struct DevProblem {
   int32_t tiles_m;             // ceil(m / 256)
   int32_t apply_tr, apply_tc;  // apply tiles per slice over rows / cols of storage
   int32_t slice_base;          // global index of this problem's first slice
-  int32_t ld_x;                // round_up(cols, 4): ld of the fp32 iterate
+  int32_t ld_x;                // round_up(cols, 32): ld of the fp32 iterate
   // per-phase workgroup prefix (first global workgroup of this problem)
   int32_t wg0[PH_COUNT];
   int32_t pad1;

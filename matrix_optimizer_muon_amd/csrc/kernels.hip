@@ -35,6 +35,12 @@ typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 
+// Global-memory (address space 1) view of a pointer.  Pointers read out of the
+// device-side problem table are generic to the compiler, which would otherwise
+// emit flat accesses (counted on both vmcnt and lgkmcnt, hence coarse waits).
+template <typename T> using gptr = __attribute__((address_space(1))) T*;
+template <typename T> __device__ __forceinline__ gptr<T> glob(T* p) { return (gptr<T>)p; }
+
 // ---------------------------------------------------------------------------
 // small helpers
 // ---------------------------------------------------------------------------
@@ -338,9 +344,13 @@ __global__ __launch_bounds__(kThreads) void k_update(LaunchTable tab, LaunchScal
 // operand read as zero through the buffer's range check).  The four 16-byte
 // chunks of a row are XOR-swizzled with (row >> 2) & 3 so that 16 consecutive
 // rows read at one logical chunk cover all 64 LDS banks.  Per stage: fragment
-// reads of the second half-step overlap the first half-step's MFMAs, then one
-// barrier hands over the next stage and its first fragments are read while the
-// second half-step's MFMAs run.
+// Ping-pong schedule: the two waves sharing a SIMD belong to different groups
+// (group = wave >> 2, the 128-row half of the tile they own), and the groups run
+// one phase apart.  A phase is either an MFMA phase (16 MFMAs on the fragments
+// of one stage) or a memory phase (wait for the stage's DMA, read all of its
+// fragments, issue the DMA of the stage three ahead); a workgroup barrier ends
+// every phase.  While one group's waves keep the matrix cores busy, the other
+// group's waves move data, so no barrier drains the MFMA pipeline.
 // ---------------------------------------------------------------------------
 constexpr int kGemmWaves = 8;
 constexpr int kGemmThreads = 64 * kGemmWaves;
@@ -388,6 +398,9 @@ __device__ __forceinline__ void mfma_chunk<float>(f32x16_t& acc, const u32x4_t& 
 // s_waitcnt with only vmcnt constrained (expcnt 7, lgkmcnt 15 = no wait)
 #define DMUON_WAIT_VM(n) __builtin_amdgcn_s_waitcnt((0x7 << 4) | (0xF << 8) | ((n) & 15) | ((((n) >> 4) & 3) << 14))
 
+// s_waitcnt with only lgkmcnt constrained to 0 (vmcnt 63, expcnt 7 = no wait)
+#define DMUON_WAIT_LGKM0() __builtin_amdgcn_s_waitcnt(0xF | (0x3 << 14) | (0x7 << 4))
+
 template <typename T>
 __device__ __forceinline__ void gemm_mainloop(const Operands& op, char* smem, f32x16_t (&acc)[4][2]) {
   const int tid = threadIdx.x, lane = tid & 63;
@@ -430,7 +443,7 @@ __device__ __forceinline__ void gemm_mainloop(const Operands& op, char* smem, f3
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
 
-  u32x4_t fa[2][4], fb[2][2];
+  u32x4_t fa[2][4], fb[2][2];     // all fragments of one stage
   auto issue = [&](int kt) {
     char* base = smem + (kt % kStages) * kStageBytes;
 #pragma unroll
@@ -443,50 +456,61 @@ __device__ __forceinline__ void gemm_mainloop(const Operands& op, char* smem, f3
                                                offb[q] + kt * kRowBytes, 0, 0, 0);
     }
   };
-  auto fload = [&](int kt, int ss, int buf) {
+  const int KT = op.ktiles;        // ≥ 2 (leading dims are multiples of 64 elements)
+  const bool lead = wr == 1;       // group 1 runs one phase ahead of group 0
+
+  // Memory phase of stage kt.  Every wave waited for its own share of stage kt
+  // in its previous memory phase (or before the first barrier), so each share
+  // a wave reads here landed before at least one barrier, like the other
+  // group's share.  Here it waits for its share of stage kt + 1; stages up to
+  // min(kt + 2, KT − 1) have been issued.
+  auto mem_phase = [&](int kt) {
+    if (kt + 2 < KT) DMUON_WAIT_VM(kDmaPerStage);
+    else DMUON_WAIT_VM(0);
     const char* base = smem + (kt % kStages) * kStageBytes;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) fa[buf][i] = *(const u32x4_t*)(base + fa_off[ss][i]);
+    for (int ss = 0; ss < 2; ++ss) {
 #pragma unroll
-    for (int j = 0; j < 2; ++j) fb[buf][j] = *(const u32x4_t*)(base + fb_off[ss][j]);
-  };
-  auto mmas = [&](int buf) {
+      for (int i = 0; i < 4; ++i) fa[ss][i] = *(const u32x4_t*)(base + fa_off[ss][i]);
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-      for (int j = 0; j < 2; ++j) mfma_chunk<T>(acc[i][j], fa[buf][i], fb[buf][j]);
-  };
-  // mode 0: steady state (issue stage kt + 3, wait for stage kt + 1 with one younger
-  // stage in flight); 1: tail (nothing left to issue, wait for everything); 2: last stage
-  auto body = [&](int kt, int mode) {
-    fload(kt, 1, 1);
-    __builtin_amdgcn_sched_barrier(0);
-    mmas(0);
-    __builtin_amdgcn_sched_barrier(0);
-    if (mode != 2) {
-      if (mode == 0) DMUON_WAIT_VM(kDmaPerStage * (kStages - 3));
-      else DMUON_WAIT_VM(0);
-      // stage kt+1 landed for every wave, and every wave is done reading stage kt-1
-      __builtin_amdgcn_s_barrier();
-      if (mode == 0) issue(kt + kStages - 1);
-      fload(kt + 1, 0, 0);
+      for (int j = 0; j < 2; ++j) fb[ss][j] = *(const u32x4_t*)(base + fb_off[ss][j]);
     }
-    __builtin_amdgcn_sched_barrier(0);
-    mmas(1);
-    __builtin_amdgcn_sched_barrier(0);
+    // the slot of stage kt − 1, read by both groups in earlier phases
+    if (kt + kStages - 1 < KT) issue(kt + kStages - 1);
+    // fragment reads complete before the barrier that releases this slot
+    DMUON_WAIT_LGKM0();
+  };
+  auto mfma_phase = [&]() {
+    __builtin_amdgcn_s_setprio(1);
+#pragma unroll
+    for (int ss = 0; ss < 2; ++ss)
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j) mfma_chunk<T>(acc[i][j], fa[ss][i], fb[ss][j]);
+    __builtin_amdgcn_s_setprio(0);
   };
 
-  const int KT = op.ktiles;   // ≥ 2 (leading dims are multiples of 64 elements)
   const int pro = KT < kStages - 1 ? KT : kStages - 1;
   for (int st = 0; st < pro; ++st) issue(st);
-  if (KT >= kStages - 1) DMUON_WAIT_VM(kDmaPerStage * (kStages - 2));
+  if (pro == 3) DMUON_WAIT_VM(2 * kDmaPerStage);      // own share of stage 0
+  else if (pro == 2) DMUON_WAIT_VM(kDmaPerStage);
   else DMUON_WAIT_VM(0);
   __builtin_amdgcn_s_barrier();
-  fload(0, 0, 0);
-  int kt = 0;
-  for (; kt + kStages - 1 < KT; ++kt) body(kt, 0);
-  for (; kt + 1 < KT; ++kt) body(kt, 1);
-  body(kt, 2);
+  if (!lead) __builtin_amdgcn_s_barrier();             // trailing group: one phase late
+  __builtin_amdgcn_sched_barrier(0);
+#pragma unroll 1
+  for (int kt = 0; kt < KT; ++kt) {
+    mem_phase(kt);
+    __builtin_amdgcn_sched_barrier(0);
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_sched_barrier(0);
+    mfma_phase();
+    __builtin_amdgcn_sched_barrier(0);
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  if (lead) __builtin_amdgcn_s_barrier();              // every wave passes 2·KT + 2 barriers
   // all LDS reads done before the caller reuses LDS
   __syncthreads();
 }
@@ -524,6 +548,298 @@ __device__ __forceinline__ int xcd_logical_block() {
   if ((w + 1) * win > G) return b;
   const int xcd = b & 7, slot = (b >> 3) - w * kXcdRun;
   return w * win + xcd * kXcdRun + slot;
+}
+
+// ---- Gram / square epilogue.  Each 128-row half of the tile is staged in LDS
+// (fp32); a row pass writes the row-major block with 8- or 16-byte vectors and a
+// column pass writes the mirrored block of an off-diagonal tile.
+//   Gram:   A' = acc − d·I
+//   square: B' = (b + 2cd)·A' + c·acc   (acc = A'·A'ᵀ = A'² since A' is symmetric)
+template <typename T, int PH>
+__device__ __forceinline__ void sym_epilogue(const DevProblem& P, const LaunchScalars& s,
+                                             f32x16_t (&acc)[4][2], char* smem, int slice, int ti,
+                                             int tj, int row0, int col0, float d) {
+  const int tid = threadIdx.x;
+  const int m = P.m, ldm = P.ld_m;
+  T* dst = (T*)(PH == PH_GRAM ? P.ap : P.bp) + (int64_t)slice * m * ldm;
+  T* dstT = ti != tj ? dst : nullptr;
+  const T* aprime = (const T*)P.ap + (int64_t)slice * m * ldm;
+  const float lin = s.b + 2.f * s.c * d;
+  const int lane = tid & 63, wave = tid >> 6;
+  const int wr = wave >> 2, wc = wave & 3, h = lane >> 5, r32 = lane & 31;
+#pragma unroll 1
+  for (int hf = 0; hf < 2; ++hf) {
+    // (1) the four waves holding rows [128·hf, 128·hf + 128) stage their accumulators
+    if (wr == hf) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int rr = i * 32 + (r >> 2) * 8 + h * 4 + (r & 3);
+            const int cc = wc * 64 + j * 32 + r32;
+            *(float*)(smem + stage_off(rr, cc)) = acc[i][j][r];
+          }
+    }
+    __syncthreads();
+    // (2) row pass: 128 rows × 64 chunks of 4 columns, in two batches of 8 chunks
+    // per thread; each batch issues all its global loads before any store, since
+    // loads and stores share one in-order completion counter.
+#pragma unroll 1
+    for (int kb = 0; kb < 16; kb += 8) {
+      float4 xin[8];
+      uint2 ain[8];
+#pragma unroll
+      for (int q = 0; q < 8; ++q) {
+        const int id = tid + kGemmThreads * (kb + q);
+        const int rr = id >> 6, cq = id & 63;
+        const int gr = row0 + hf * 128 + rr, gc = col0 + 4 * cq;
+        xin[q] = make_float4(0.f, 0.f, 0.f, 0.f);
+        ain[q] = make_uint2(0u, 0u);
+        if (PH == PH_SQUARE && gr < m && gc < ldm) {
+          if (sizeof(T) == 2) ain[q] = *(const uint2*)(aprime + (int64_t)gr * ldm + gc);
+          else xin[q] = *(const float4*)(aprime + (int64_t)gr * ldm + gc);
+        }
+      }
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int q = 0; q < 8; ++q) {
+        const int id = tid + kGemmThreads * (kb + q);
+        const int rr = id >> 6, cq = id & 63;
+        float* sp = (float*)(smem + rr * 1024 + ((cq ^ ((rr >> 3) & 15)) << 4));
+        const float4 a4 = *(const float4*)sp;
+        float v[4] = {a4.x, a4.y, a4.z, a4.w};
+        const int gr = row0 + hf * 128 + rr, gc = col0 + 4 * cq;
+        const bool rok = gr < m;
+        if (PH == PH_GRAM) {
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            if (gr == gc + e && rok) v[e] -= d;
+        } else {
+          float ap[4];
+          if (sizeof(T) == 2) {
+            ap[0] = __uint_as_float(ain[q].x << 16); ap[1] = __uint_as_float(ain[q].x & 0xffff0000u);
+            ap[2] = __uint_as_float(ain[q].y << 16); ap[3] = __uint_as_float(ain[q].y & 0xffff0000u);
+          } else {
+            ap[0] = xin[q].x; ap[1] = xin[q].y; ap[2] = xin[q].z; ap[3] = xin[q].w;
+          }
+#pragma unroll
+          for (int e = 0; e < 4; ++e) v[e] = fmaf(lin, ap[e], s.c * v[e]);
+        }
+        if (rok && gc < ldm) store4(dst + (int64_t)gr * ldm + gc, v[0], v[1], v[2], v[3]);
+        if (dstT) *(float4*)sp = make_float4(v[0], v[1], v[2], v[3]);
+      }
+    }
+    __syncthreads();
+    // (3) column pass: rows of the mirrored block = tile columns
+    if (dstT) {
+      constexpr int RPC = 16 / (int)sizeof(T);          // rows per 16-byte chunk
+      constexpr int CPC = 128 / RPC;                    // chunks per column (this half)
+#pragma unroll 2
+      for (int k = 0; k < (256 * CPC) / kGemmThreads; ++k) {
+        const int id = tid + kGemmThreads * k;
+        const int cc = id / CPC, rg = id % CPC;
+        const int trow = col0 + cc;
+        const int tcol = row0 + hf * 128 + rg * RPC;
+        if (trow >= m || tcol >= ldm) continue;
+        float v[RPC];
+#pragma unroll
+        for (int e = 0; e < RPC; ++e) v[e] = *(const float*)(smem + stage_off(rg * RPC + e, cc));
+        store_row16(dstT + (int64_t)trow * ldm + tcol, v);
+      }
+    }
+    __syncthreads();
+  }
+}
+
+// bf16 pair (lo, hi) packed into one dword, round to nearest even
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  const f32x2_t v = {lo, hi};
+  const bf16x2_t b = __builtin_convertvector(v, bf16x2_t);
+  uint32_t u;
+  __builtin_memcpy(&u, &b, 4);
+  return u;
+}
+// value of the neighbouring lane (lane ^ 1)
+__device__ __forceinline__ float swap_adjacent(float x) {
+  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0xB1, 0xF, 0xF, false));
+}
+
+// Buffer resource over [p, p + bytes) (a null p gives an empty range).  Buffer
+// accesses are range checked: a load beyond the range reads zero and a store
+// beyond it is dropped, which replaces per-element predicates (and the branches
+// they would need) in the apply epilogue.
+constexpr unsigned kOob = 0x7ffffff0u;       // an offset beyond every range used here
+// The fields are workgroup-uniform; readfirstlane tells the compiler so (a
+// descriptor it cannot prove uniform is rebuilt per lane in a loop).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t range_rsrc(const void* p, int64_t bytes) {
+  const uint64_t a = (uint64_t)(uintptr_t)p;
+  const unsigned lo = __builtin_amdgcn_readfirstlane((unsigned)a);
+  const unsigned hi = __builtin_amdgcn_readfirstlane((unsigned)(a >> 32));
+  const int n = __builtin_amdgcn_readfirstlane(p ? (int)bytes : 0);
+  return __builtin_amdgcn_make_buffer_rsrc((void*)(((uint64_t)hi << 32) | lo), 0, n, 0x00020000);
+}
+__device__ __forceinline__ float buf_ld(__amdgpu_buffer_rsrc_t r, unsigned off) {
+  return __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(r, (int)off, 0, 0));
+}
+__device__ __forceinline__ void buf_st(__amdgpu_buffer_rsrc_t r, unsigned off, float v) {
+  __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v), r, (int)off, 0, 0);
+}
+__device__ __forceinline__ void buf_st(__amdgpu_buffer_rsrc_t r, unsigned off, uint32_t v) {
+  __builtin_amdgcn_raw_buffer_store_b32(v, r, (int)off, 0, 0);
+}
+typedef unsigned u32x2_t __attribute__((ext_vector_type(2)));
+
+// ---- apply epilogue, in the accumulator layout (no LDS, no barrier, no branch).
+// Lane (h, r32) of wave (wr, wc) holds, for block (i, j) and register r = 4·rq + e,
+// the element at tile row 128·wr + 32·i + 8·rq + 4·h + e and tile column
+// 64·wc + 32·j + r32.  Per block:
+//   X' = α·X + acc (fp32 iterate, read and written with 4-byte accesses: each
+//        wave instruction covers two 128-byte row segments), α = a + b·d + c·d²
+//   t < k−1: the row-major operand copy, two columns per dword (even lanes take
+//        rows e = 0, 2 from their odd neighbour, odd lanes rows 1, 3), and the
+//        transposed copy, four consecutive rows per store; Σ X'² partial
+//   last:  W ← (1 − lr·wd)·W − lr·X', optional copy of X' to the output.
+// The fp32 loads run ahead of the arithmetic by three blocks (two on the last
+// apply).  All ranges start at the tile's first row (byte offsets then fit in
+// 32 bits); rows past the matrix fall outside them, columns past it get the
+// kOob offset.  Out-of-range rows and columns hold zero in acc (zero-filled
+// operands) and read X as zero, so the zero padding of the operand copies is
+// rewritten with zeros.
+template <typename T, bool LAST>
+__device__ __forceinline__ void apply_epilogue(const DevProblem& P, const LaunchScalars& s,
+                                               f32x16_t (&acc)[4][2], int slice, int u, int row0,
+                                               int col0, float d, float* red) {
+  constexpr int kAhead = LAST ? 2 : 3;
+  constexpr unsigned E = sizeof(T);
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int wr = wave >> 2, wc = wave & 3, h = lane >> 5, r32 = lane & 31;
+  const int rows = P.rows, cols = P.cols;
+  const float alpha = s.a + s.b * d + s.c * d * d;
+  const unsigned ldx = (unsigned)P.ld_x;
+  const int trows = rows - row0 < kTile ? rows - row0 : kTile;
+  const int tcols = cols - col0 < kTile ? cols - col0 : kTile;
+  const unsigned lr0 = (unsigned)(wr * 128 + h * 4);   // tile row of register e = 0 (i = rq = 0)
+  const int lc0 = wc * 64 + r32;                        // tile column of block j = 0
+  const bool odd = (lane & 1) != 0;
+
+  const __amdgpu_buffer_rsrc_t rx =
+      range_rsrc(P.xf + ((int64_t)slice * rows + row0) * ldx, (int64_t)trows * ldx * 4);
+  unsigned xo[2];                                       // byte offset of (row lr0, block j)
+#pragma unroll
+  for (int j = 0; j < 2; ++j)
+    xo[j] = lc0 + 32 * j < tcols ? (lr0 * ldx + (unsigned)(col0 + lc0 + 32 * j)) * 4u : kOob;
+
+  __amdgpu_buffer_rsrc_t rw = rx, ro = rx, rd = rx, rt = rx;
+  unsigned wo[2] = {0, 0}, dofs[2] = {0, 0}, tofs[2] = {0, 0};
+  unsigned ld_s = 0, ld_t = 0;
+  if (LAST) {
+    const int64_t first = ((int64_t)slice * rows + row0) * cols, bytes = (int64_t)trows * cols * 4;
+    rw = range_rsrc(s.write_master ? P.master + first : nullptr, bytes);
+    ro = range_rsrc(P.out ? P.out + first : nullptr, bytes);
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+      wo[j] = lc0 + 32 * j < tcols ? (lr0 * (unsigned)cols + (unsigned)(col0 + lc0 + 32 * j)) * 4u : kOob;
+  } else {
+    ld_s = (unsigned)(P.wide ? P.ld_n : P.ld_m);
+    ld_t = (unsigned)(P.wide ? P.ld_m : P.ld_n);
+    void* xa_next = (s.t & 1) ? P.xa0 : P.xa1;
+    const T* dst = (const T*)(P.wide ? P.xg : xa_next) + (int64_t)slice * rows * ld_s;
+    const T* dstT = (const T*)(P.wide ? xa_next : P.xg) + (int64_t)slice * cols * ld_t;
+    rd = range_rsrc(dst + (int64_t)row0 * ld_s, (int64_t)trows * ld_s * E);
+    rt = range_rsrc(dstT + (int64_t)col0 * ld_t, (int64_t)tcols * ld_t * E);
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      // row-major copy: the lane's dword starts at an even column
+      const unsigned gc = (unsigned)(col0 + lc0 + 32 * j);
+      const unsigned gce = E == 2 ? (gc & ~1u) : gc;
+      dofs[j] = gce < ld_s ? ((lr0 + (E == 2 && odd ? 1u : 0u)) * ld_s + gce) * E : kOob;
+      // transposed copy: row (lc0 + 32 j) of the range, columns from row0 + lr0
+      tofs[j] = ((unsigned)(lc0 + 32 * j) * ld_t + (unsigned)row0 + lr0) * E;
+    }
+  }
+
+  float xin[kAhead][16];
+  float win[LAST ? kAhead : 1][16];
+  auto load_blk = [&](int blk, int slot) {
+    const int i = blk >> 1, j = blk & 1;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const unsigned rr = (unsigned)(32 * i + 8 * (r >> 2) + (r & 3));
+      xin[slot][r] = buf_ld(rx, xo[j] + rr * ldx * 4u);
+      if (LAST) win[LAST ? slot : 0][r] = buf_ld(rw, wo[j] + rr * (unsigned)cols * 4u);
+    }
+  };
+
+  float sq = 0.f;
+#pragma unroll
+  for (int b = 0; b < kAhead; ++b) load_blk(b, b);
+#pragma unroll
+  for (int blk = 0; blk < 8; ++blk) {
+    const int slot = blk % kAhead;
+    const int i = blk >> 1, j = blk & 1;
+    float v[16];
+#pragma unroll
+    for (int r = 0; r < 16; ++r) v[r] = fmaf(alpha, xin[slot][r], acc[i][j][r]);
+    if (LAST) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const unsigned rr = (unsigned)(32 * i + 8 * (r >> 2) + (r & 3));
+        const unsigned o = wo[j] + rr * (unsigned)cols * 4u;
+        buf_st(ro, o, v[r]);
+        buf_st(rw, o, fmaf(-s.lr, v[r], s.decay * win[LAST ? slot : 0][r]));
+      }
+    } else {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const unsigned rr = (unsigned)(32 * i + 8 * (r >> 2) + (r & 3));
+        buf_st(rx, xo[j] + rr * ldx * 4u, v[r]);
+        sq = fmaf(v[r], v[r], sq);
+      }
+      // transposed copy: four consecutive rows of one column per store
+#pragma unroll
+      for (int rq = 0; rq < 4; ++rq) {
+        const unsigned rr = (unsigned)(32 * i + 8 * rq);
+        const unsigned o = (unsigned)row0 + lr0 + rr < ld_t ? tofs[j] + rr * E : kOob;
+        if constexpr (E == 2) {
+          const u32x2_t w2 = {pack_bf16x2(v[4 * rq], v[4 * rq + 1]), pack_bf16x2(v[4 * rq + 2], v[4 * rq + 3])};
+          __builtin_amdgcn_raw_buffer_store_b64(w2, rt, (int)o, 0, 0);
+        } else {
+          const u32x4_t w4 = {__float_as_uint(v[4 * rq]), __float_as_uint(v[4 * rq + 1]),
+                              __float_as_uint(v[4 * rq + 2]), __float_as_uint(v[4 * rq + 3])};
+          __builtin_amdgcn_raw_buffer_store_b128(w4, rt, (int)o, 0, 0);
+        }
+      }
+      // row-major copy
+#pragma unroll
+      for (int rq = 0; rq < 4; ++rq) {
+        if constexpr (E == 2) {
+#pragma unroll
+          for (int pe = 0; pe < 2; ++pe) {        // register pair (2pe, 2pe + 1)
+            const float v0 = v[4 * rq + 2 * pe], v1 = v[4 * rq + 2 * pe + 1];
+            const float got = swap_adjacent(odd ? v0 : v1);
+            const unsigned rr = (unsigned)(32 * i + 8 * rq + 2 * pe);
+            buf_st(rd, dofs[j] + rr * ld_s * E, odd ? pack_bf16x2(got, v1) : pack_bf16x2(v0, got));
+          }
+        } else {
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const unsigned rr = (unsigned)(32 * i + 8 * rq + e);
+            buf_st(rd, dofs[j] + rr * ld_s * E, v[4 * rq + e]);
+          }
+        }
+      }
+    }
+    if (blk + kAhead < 8) load_blk(blk + kAhead, slot);
+  }
+  if (!LAST) {
+    const float tot = block_sum<kGemmWaves>(sq, red);
+    if (threadIdx.x == 0) P.part_apply[(int64_t)slice * P.apply_tr * P.apply_tc + u] = tot;
+  }
 }
 
 template <typename T, int PH, bool LAST>
@@ -592,189 +908,11 @@ __global__ __launch_bounds__(kGemmThreads) void k_gemm(LaunchTable tab, LaunchSc
 
   f32x16_t acc[4][2];
   gemm_mainloop<T>(op, smem, acc);
-
-  // ---- epilogue: each 128-row half of the tile is staged in LDS (fp32), then a
-  // row pass does the row-major global I/O with 16-byte vectors and a column pass
-  // writes the transposed copy (apply) or the mirrored block (Gram, square).
-  const int tid = threadIdx.x;
-  const int ldm = P.ld_m;
-  T* dst = nullptr;            // row-major destination (Gram: A', square: B', apply: straight copy)
-  T* dstT = nullptr;           // transposed destination (mirror / transposed copy)
-  int ld_dst = 0, ld_t = 0, rows_lim = 0, cols_lim = 0, ldst_lim = 0, t_rows_lim = 0;
-  const T* aprime = nullptr;
-  float alpha = 0.f, lin = 0.f;
-  const int rows = P.rows, cols = P.cols;
-  float* xf = nullptr;
-  float* wst = nullptr;
-  float* outp = nullptr;
-  bool vec_user = false;
-  if (PH == PH_GRAM || PH == PH_SQUARE) {
-    dst = (T*)(PH == PH_GRAM ? P.ap : P.bp) + (int64_t)slice * m * ldm;
-    dstT = ti != tj ? dst : nullptr;
-    ld_dst = ld_t = ldm;
-    rows_lim = m;          // valid output rows
-    cols_lim = m;          // valid output cols (values beyond are zero)
-    ldst_lim = ldm;        // columns written (zero padding up to ld)
-    t_rows_lim = m;        // rows of the transposed destination
-    aprime = (const T*)P.ap + (int64_t)slice * m * ldm;
-    lin = s.b + 2.f * s.c * d;
+  if constexpr (PH == PH_APPLY) {
+    apply_epilogue<T, LAST>(P, s, acc, slice, u, row0, col0, d, red);
   } else {
-    alpha = s.a + s.b * d + s.c * d * d;
-    xf = P.xf + (int64_t)slice * rows * P.ld_x;
-    rows_lim = rows;
-    cols_lim = cols;
-    if (LAST) {
-      const int64_t per = (int64_t)rows * cols;
-      wst = s.write_master ? P.master + (int64_t)slice * per : nullptr;
-      outp = P.out ? P.out + (int64_t)slice * per : nullptr;
-      vec_user = (cols & 3) == 0 && (!wst || ((uintptr_t)wst & 15) == 0) &&
-                 (!outp || ((uintptr_t)outp & 15) == 0);
-    } else {
-      const int ld_s = P.wide ? P.ld_n : P.ld_m;
-      ld_t = P.wide ? P.ld_m : P.ld_n;
-      void* xa_next = (s.t & 1) ? P.xa0 : P.xa1;
-      dst = (T*)(P.wide ? P.xg : xa_next) + (int64_t)slice * rows * ld_s;
-      dstT = (T*)(P.wide ? xa_next : P.xg) + (int64_t)slice * cols * ld_t;
-      ld_dst = ld_s;
-      ldst_lim = ld_s;
-      t_rows_lim = cols;
-    }
+    sym_epilogue<T, PH>(P, s, acc, smem, slice, ti, tj, row0, col0, d);
   }
-  float acc_sq = 0.f;
-  const int lane = tid & 63, wave = tid >> 6;
-  const int wr = wave >> 2, wc = wave & 3, h = lane >> 5, r32 = lane & 31;
-#pragma unroll 1
-  for (int hf = 0; hf < 2; ++hf) {
-    // (1) the four waves holding rows [128·hf, 128·hf + 128) stage their accumulators
-    if (wr == hf) {
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int j = 0; j < 2; ++j)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int rr = i * 32 + (r >> 2) * 8 + h * 4 + (r & 3);
-            const int cc = wc * 64 + j * 32 + r32;
-            *(float*)(smem + stage_off(rr, cc)) = acc[i][j][r];
-          }
-    }
-    __syncthreads();
-    // (2) row pass: 128 rows × 64 chunks of 4 columns, in two batches of 8 chunks
-    // per thread; each batch issues all its global loads before any store, since
-    // loads and stores share one in-order completion counter.
-#pragma unroll 1
-    for (int kb = 0; kb < 16; kb += 8) {
-      float4 xin[8], win[LAST ? 8 : 1];
-      uint2 ain[8];
-#pragma unroll
-      for (int q = 0; q < 8; ++q) {
-        const int id = tid + kGemmThreads * (kb + q);
-        const int rr = id >> 6, cq = id & 63;
-        const int gr = row0 + hf * 128 + rr, gc = col0 + 4 * cq;
-        const bool rok = gr < rows_lim;
-        xin[q] = make_float4(0.f, 0.f, 0.f, 0.f);
-        if (LAST) win[LAST ? q : 0] = make_float4(0.f, 0.f, 0.f, 0.f);
-        ain[q] = make_uint2(0u, 0u);
-        if (PH == PH_SQUARE) {
-          if (rok && gc < ldm) {
-            if (sizeof(T) == 2) ain[q] = *(const uint2*)(aprime + (int64_t)gr * ldm + gc);
-            else xin[q] = *(const float4*)(aprime + (int64_t)gr * ldm + gc);
-          }
-        } else if (PH == PH_APPLY) {
-          if (rok && gc < cols) {
-            xin[q] = *(const float4*)(xf + (int64_t)gr * P.ld_x + gc);
-            if (LAST && wst && vec_user) win[LAST ? q : 0] = *(const float4*)(wst + (int64_t)gr * cols + gc);
-          }
-        }
-      }
-      __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-      for (int q = 0; q < 8; ++q) {
-        const int id = tid + kGemmThreads * (kb + q);
-        const int rr = id >> 6, cq = id & 63;
-        float* sp = (float*)(smem + rr * 1024 + ((cq ^ ((rr >> 3) & 15)) << 4));
-        const float4 a4 = *(const float4*)sp;
-        float v[4] = {a4.x, a4.y, a4.z, a4.w};
-        const int gr = row0 + hf * 128 + rr, gc = col0 + 4 * cq;
-        const bool rok = gr < rows_lim;
-        if (PH == PH_GRAM) {
-#pragma unroll
-          for (int e = 0; e < 4; ++e)
-            if (gr == gc + e && rok) v[e] -= d;
-        } else if (PH == PH_SQUARE) {
-          float ap[4];
-          if (sizeof(T) == 2) {
-            ap[0] = __uint_as_float(ain[q].x << 16); ap[1] = __uint_as_float(ain[q].x & 0xffff0000u);
-            ap[2] = __uint_as_float(ain[q].y << 16); ap[3] = __uint_as_float(ain[q].y & 0xffff0000u);
-          } else {
-            ap[0] = xin[q].x; ap[1] = xin[q].y; ap[2] = xin[q].z; ap[3] = xin[q].w;
-          }
-#pragma unroll
-          for (int e = 0; e < 4; ++e) v[e] = fmaf(lin, ap[e], s.c * v[e]);
-        } else {
-          const float x[4] = {xin[q].x, xin[q].y, xin[q].z, xin[q].w};
-#pragma unroll
-          for (int e = 0; e < 4; ++e) v[e] = (rok && gc + e < cols) ? fmaf(alpha, x[e], v[e]) : 0.f;
-          if (LAST) {
-            if (rok && gc < cols) {
-              if (vec_user) {
-                const int64_t o = (int64_t)gr * cols + gc;
-                if (outp) *(float4*)(outp + o) = make_float4(v[0], v[1], v[2], v[3]);
-                if (wst) {
-                  float4 w4 = win[LAST ? q : 0];
-                  w4.x = fmaf(-s.lr, v[0], s.decay * w4.x);
-                  w4.y = fmaf(-s.lr, v[1], s.decay * w4.y);
-                  w4.z = fmaf(-s.lr, v[2], s.decay * w4.z);
-                  w4.w = fmaf(-s.lr, v[3], s.decay * w4.w);
-                  *(float4*)(wst + o) = w4;
-                }
-              } else {
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                  if (gc + e >= cols) break;
-                  const int64_t o = (int64_t)gr * cols + gc + e;
-                  if (outp) outp[o] = v[e];
-                  if (wst) wst[o] = fmaf(-s.lr, v[e], s.decay * wst[o]);
-                }
-              }
-            }
-            continue;
-          }
-          if (rok && gc < cols) {
-            *(float4*)(xf + (int64_t)gr * P.ld_x + gc) = make_float4(v[0], v[1], v[2], v[3]);
-#pragma unroll
-            for (int e = 0; e < 4; ++e) acc_sq = fmaf(v[e], v[e], acc_sq);
-          }
-        }
-        if (rok && gc < (PH == PH_APPLY ? ldst_lim : ldm)) store4(dst + (int64_t)gr * ld_dst + gc, v[0], v[1], v[2], v[3]);
-        if (dstT) *(float4*)sp = make_float4(v[0], v[1], v[2], v[3]);
-      }
-    }
-    __syncthreads();
-    // (3) column pass: transposed destination rows = tile columns
-    if (dstT) {
-      constexpr int RPC = 16 / (int)sizeof(T);          // rows per 16-byte chunk
-      constexpr int CPC = 128 / RPC;                    // chunks per column (this half)
-#pragma unroll 2
-      for (int k = 0; k < (256 * CPC) / kGemmThreads; ++k) {
-        const int id = tid + kGemmThreads * k;
-        const int cc = id / CPC, rg = id % CPC;
-        const int trow = col0 + cc;                       // row of the transposed destination
-        const int tcol = row0 + hf * 128 + rg * RPC;      // first column written
-        if (trow >= t_rows_lim || tcol >= (PH == PH_APPLY ? ld_t : ldm)) continue;
-        float v[RPC];
-#pragma unroll
-        for (int e = 0; e < RPC; ++e) v[e] = *(const float*)(smem + stage_off(rg * RPC + e, cc));
-        store_row16(dstT + (int64_t)trow * (PH == PH_APPLY ? ld_t : ldm) + tcol, v);
-      }
-    }
-    __syncthreads();
-  }
-  if (PH == PH_APPLY && !LAST) {
-    const float tot = block_sum<kGemmWaves>(acc_sq, red);
-    if (threadIdx.x == 0) P.part_apply[(int64_t)slice * P.apply_tr * P.apply_tc + u] = tot;
-  }
-  (void)cols_lim;
 }
 
 // plain C = A·Bᵀ (fp32 out) on the same core: the contraction test hook
