@@ -343,7 +343,8 @@ __global__ __launch_bounds__(kThreads) void k_update(LaunchTable tab, LaunchScal
 // deep, filled by buffer_load … lds (global → LDS without VGPRs; rows beyond the
 // operand read as zero through the buffer's range check).  The four 16-byte
 // chunks of a row are XOR-swizzled with (row >> 2) & 3 so that 16 consecutive
-// rows read at one logical chunk cover all 64 LDS banks.  Per stage: fragment
+// rows read at one logical chunk cover all 64 LDS banks.
+//
 // Ping-pong schedule: the two waves sharing a SIMD belong to different groups
 // (group = wave >> 2, the 128-row half of the tile they own), and the groups run
 // one phase apart.  A phase is either an MFMA phase (16 MFMAs on the fragments
