@@ -540,15 +540,17 @@ __device__ __forceinline__ void tri_tile(int u, int T, int& ti, int& tj) {
 // window each XCD takes kXcdRun consecutive tiles (neighbours share operand
 // panels in that XCD's L2), and all XCDs advance through the list together, so
 // tiles of unequal cost (long-K problems first) are spread over every XCD.  A
-// last partial window keeps the identity map; the map is a bijection on [0, G).
+// last partial window of R tiles is split the same way into 8 contiguous runs
+// (the first R % 8 XCDs take one tile more).  The map is a bijection on [0, G).
 constexpr int kXcdRun = 32;
 __device__ __forceinline__ int xcd_logical_block() {
   const int G = gridDim.x, b = blockIdx.x;
   constexpr int win = 8 * kXcdRun;
   const int w = b / win;
-  if ((w + 1) * win > G) return b;
   const int xcd = b & 7, slot = (b >> 3) - w * kXcdRun;
-  return w * win + xcd * kXcdRun + slot;
+  if ((w + 1) * win <= G) return w * win + xcd * kXcdRun + slot;
+  const int R = G - w * win, per = R >> 3, rem = R & 7;
+  return w * win + (xcd < rem ? xcd * (per + 1) : rem * (per + 1) + (xcd - rem) * per) + slot;
 }
 
 // ---- Gram / square epilogue.  Each 128-row half of the tile is staged in LDS
