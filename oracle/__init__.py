@@ -1,4 +1,4 @@
-"""Plain, slow fp64 CPU oracle for the owner-rank Muon step (test infrastructure).
+"""Plain, slow fp64 CPU oracle for the owner-rank optimizer step (test infrastructure).
 
 This package is TEST INFRASTRUCTURE ONLY.  Only ``tests/``,
 ``__graft_entry__.smoke()`` and the ``cpu_baseline`` leg of ``bench.py`` may
@@ -19,5 +19,7 @@ from .muon import (  # noqa: F401
     decay_update,
     muon_step,
     validate_ndim,
+    publish_bf16,
 )
+from .adamw import adamw_step  # noqa: F401
 from .lpt import lpt_assign, per_layer_lpt  # noqa: F401

@@ -52,15 +52,21 @@ def validate_ndim(shape) -> None:
         raise ValueError(f"Muon needs a tensor with >= 2 dims, got shape {tuple(shape)}")
 
 
-def momentum_update(B, G, mu):
-    """B ← μ·B + G in fp64.
+def momentum_update(B, G, mu, grad_scale=1.0):
+    """B ← μ·B + s·G in fp64.
 
     DMuon architecture page §2 (the owner's step includes momentum) and the HSDP
     guide ("what happens underneath": the owner holds the momentum buffer).  The
     heavy-ball form without dampening is the reading taken (the pages name only
     "momentum").
+
+    s is the gradient-ingest scale.  The pages reduce gradients to the owner with
+    an averaging reduce whose net divisor is the number of contributing ranks
+    (HSDP guide, "两阶段梯度 Reduce" / two-stage gradient reduce); an owner that
+    receives a summed buffer instead applies s = 1/N here.  s = 1 for an
+    already-averaged gradient.
     """
-    return mu * np.asarray(B, dtype=np.float64) + np.asarray(G, dtype=np.float64)
+    return mu * np.asarray(B, dtype=np.float64) + grad_scale * np.asarray(G, dtype=np.float64)
 
 
 def frobenius_normalize(X, eps):
@@ -133,7 +139,7 @@ def decay_update(W, O, lr, wd):
     return (1.0 - lr * wd) * W - lr * np.asarray(O, dtype=np.float64)
 
 
-def muon_step(G, B, W, *, lr, mu, wd, eps, a, b, c, steps):
+def muon_step(G, B, W, *, lr, mu, wd, eps, a, b, c, steps, grad_scale=1.0):
     """One owner-rank Muon step on one tensor; returns (B_new, O, W_new) in fp64.
 
     Order: momentum → NS (per 2-D slice over the last two dims) → decay + update.
@@ -143,7 +149,33 @@ def muon_step(G, B, W, *, lr, mu, wd, eps, a, b, c, steps):
     validate_ndim(np.shape(G))
     if np.shape(G) != np.shape(B) or np.shape(G) != np.shape(W):
         raise ValueError("G, B and W must have the same shape")
-    B_new = momentum_update(B, G, mu)
+    B_new = momentum_update(B, G, mu, grad_scale)
     O = newton_schulz_batched(B_new, a, b, c, steps, eps, normalize=True)
     W_new = decay_update(W, O, lr, wd)
     return B_new, O, W_new
+
+
+def publish_bf16(W32):
+    """bf16 bits (uint16) of fp32 values, rounded to nearest, ties to even.
+
+    The publish step: after the update the owner broadcasts its parameter in
+    ``param_dtype`` (bf16 in the pages' policy example), cast from the fp32
+    master (routing page, dtype paragraph: ``param_dtype`` is the forward
+    parameter / communication dtype, ``master_dtype`` the storage precision;
+    architecture page §2: the owner broadcasts ``_owned_data`` before forward).
+
+    Written from the definition of the format: bf16 keeps the upper 16 bits of
+    the fp32 encoding; the discarded 16 bits round the kept part to nearest,
+    and an exact half rounds to the even kept value.  NaN stays a (quiet) NaN.
+    Overflow past the largest finite bf16 carries into the exponent and gives
+    infinity, as rounding to nearest requires.
+    """
+    u = np.ascontiguousarray(W32, dtype=np.float32).view(np.uint32).astype(np.uint64)
+    upper = u >> 16
+    lower = u & 0xFFFF
+    half = 0x8000
+    round_up = (lower > half) | ((lower == half) & ((upper & 1) == 1))
+    out = (upper + round_up.astype(np.uint64)) & 0xFFFF
+    is_nan = ((u >> 23) & 0xFF == 0xFF) & ((u & 0x7FFFFF) != 0)
+    out = np.where(is_nan, upper | 0x40, out)
+    return out.astype(np.uint16)
