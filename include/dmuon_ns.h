@@ -7,12 +7,15 @@
  *
  *   for every owned gradient tensor G (2-D, or 3-D = a batch of matrices over
  *   the last two dims), with momentum buffer B and fp32 master weight W:
- *     B ← μ·B + G
+ *     B ← μ·B + s·G                       (s: gradient-ingest scale, 1 or 1/N)
  *     for each 2-D slice: X₀ = B_slice / (‖B_slice‖_F + eps), oriented so that
  *       the Gram matrix is on the short side (a slice with rows > cols is
  *       treated as its transpose); then k times
  *       X ← a·X + b·(X Xᵀ) X + c·(X Xᵀ)² X;  O = X (original orientation)
- *     W ← (1 − lr·wd)·W − lr·O
+ *     W ← (1 − lr·wd)·W − lr·O;  optionally P = bf16(W) (the published copy)
+ *
+ *   and, for the owner's small and 1-D parameters (the "adamw" route), one
+ *   AdamW step per element (dmuon_adamw_step).
  *
  *   DMuon "架构设计" (Architecture design) page, §1 (the Newton–Schulz
  *   equation with coefficients α, β, γ = a, b, c) and §2 (the owner alone runs
@@ -76,12 +79,19 @@ typedef enum { DMUON_PREC_BF16_MFMA = 0, DMUON_PREC_F32 = 1 } dmuon_prec;
 /* One owned parameter.  shape = (rows, cols) for ndim 2 or (batch, rows, cols)
  * for ndim 3 (only shape[0..ndim-1] are read).  Every dim must be ≥ 0 and
  * rows, cols ≤ 65536; a tensor with a zero dim is skipped (no-op).
- *   grad      device, read-only, grad_dtype (bf16 or fp32), the averaged gradient
- *   momentum  device fp32, updated in place (B ← μB + G)
- *   master    device fp32, updated in place (W ← (1 − lr·wd)W − lr·O)
- *   ns_out    device fp32 or NULL: if set, receives O (same shape) as well
- * grad must not overlap momentum, master or ns_out; momentum, master and ns_out
- * must not overlap each other or another tensor's buffers (DMUON_E_ALIAS). */
+ *   grad       device, read-only, grad_dtype (bf16 or fp32): the reduced gradient,
+ *              read in place (it may sit inside the owner's packed reduce buffer)
+ *   momentum   device fp32, updated in place (B ← μB + s·G)
+ *   master     device fp32, updated in place (W ← (1 − lr·wd)W − lr·O)
+ *   ns_out     device fp32 or NULL: if set, receives O (same shape) as well
+ *   param_out  device bf16 (raw 16-bit words) or NULL: if set, receives the
+ *              updated master rounded to nearest-even bf16, same shape (the
+ *              parameter the owner publishes: routing page, dtype paragraph,
+ *              param_dtype; architecture page §2, owner broadcast); it may sit
+ *              inside the owner's packed broadcast buffer
+ * grad must not overlap momentum, master, ns_out or param_out; the written
+ * buffers must not overlap each other or another tensor's buffers
+ * (DMUON_E_ALIAS). */
 typedef struct {
   int32_t ndim;
   int32_t grad_dtype;       /* dmuon_dtype */
@@ -90,12 +100,15 @@ typedef struct {
   float* momentum;
   float* master;
   float* ns_out;
+  uint16_t* param_out;
 } dmuon_tensor;
 
 /* Step hyper-parameters.  lr, momentum (μ), weight_decay (wd): the HSDP guide's
  * example builds the optimizer with lr 0.02 and momentum 0.95.  eps ≥ 0 is added
  * to the Frobenius norm.  (a, b, c) are the page's (α, β, γ).  0 ≤ ns_steps ≤ 64.
- * prec is a dmuon_prec. */
+ * prec is a dmuon_prec.  grad_scale (s, finite) multiplies the gradient as it is
+ * read: 1 for an averaged reduce, 1/N for a summed one (HSDP guide, two-stage
+ * gradient reduce: the net divisor is the number of contributing ranks). */
 typedef struct {
   float lr;
   float momentum;
@@ -104,6 +117,7 @@ typedef struct {
   float a, b, c;
   int32_t ns_steps;
   int32_t prec;
+  float grad_scale;
 } dmuon_step_cfg;
 
 /* Bytes of workspace dmuon_muon_step needs for these tensors and cfg (host only,
@@ -163,6 +177,55 @@ int dmuon_lpt_assign(int64_t n, const int64_t* rows, const int64_t* cols, const 
                      int64_t* owner_order, int64_t* n_owned, int64_t* group_offsets,
                      int32_t* n_groups);
 
+/* ---- the "adamw" route ----------------------------------------------------
+ * Routing page, route table: "adamw" runs AdamW on the owner for LayerNorm
+ * weights, biases and other small parameters, which the owner then broadcasts;
+ * the MindSpore parameter-grouping page §1 / §2.1 sends 1-D parameters to an
+ * element-wise optimizer.  The pages do not restate AdamW; the step is the
+ * published AdamW (decoupled weight decay, bias-corrected moments):
+ *   g ← s·G;  p ← (1 − lr·wd)·p;  m ← β₁m + (1 − β₁)g;  v ← β₂v + (1 − β₂)g²
+ *   p ← p − lr·m̂ / (√v̂ + eps),  m̂ = m / (1 − β₁ᵗ),  v̂ = v / (1 − β₂ᵗ)
+ * in fp32, element by element; optionally P = bf16(p) (round to nearest even). */
+
+/* One parameter of any shape, dense, numel ≥ 0 elements (0: skipped).
+ *   grad        device, read-only, grad_dtype (bf16 or fp32)
+ *   param       device fp32, updated in place
+ *   exp_avg     device fp32 (m), updated in place
+ *   exp_avg_sq  device fp32 (v), updated in place
+ *   param_out   device bf16 (raw 16-bit words) or NULL: the published copy
+ * Same overlap rules as dmuon_tensor (DMUON_E_ALIAS). */
+typedef struct {
+  int64_t numel;
+  int32_t grad_dtype;       /* dmuon_dtype */
+  int32_t reserved;         /* must be 0 */
+  const void* grad;
+  float* param;
+  float* exp_avg;
+  float* exp_avg_sq;
+  uint16_t* param_out;
+} dmuon_adamw_tensor;
+
+/* lr ≥ 0, 0 ≤ beta1, beta2 < 1, eps > 0, weight_decay, grad_scale finite;
+ * step ≥ 1 is the step number the bias correction uses (the first step is 1). */
+typedef struct {
+  float lr;
+  float beta1;
+  float beta2;
+  float eps;
+  float weight_decay;
+  float grad_scale;
+  int32_t step;
+} dmuon_adamw_cfg;
+
+/* Bytes of workspace dmuon_adamw_step needs (host only, no HIP call). */
+int dmuon_adamw_step_workspace_size(const dmuon_adamw_tensor* tensors, int32_t n_tensors, size_t* bytes);
+
+/* One AdamW step over n_tensors tensors in one grouped launch (asynchronous on
+ * stream).  n_tensors ≥ 0; tensors may be NULL only when n_tensors is 0.  The
+ * workspace (device, 256-byte aligned, ≥ the size above) is scratch. */
+int dmuon_adamw_step(const dmuon_adamw_tensor* tensors, int32_t n_tensors, const dmuon_adamw_cfg* cfg,
+                     void* workspace, size_t workspace_bytes, void* stream);
+
 /* Plain NT product C = A·Bᵀ on the matrix-core kernel the step uses (a test hook
  * for the contraction core).  A: M×K (lda elements per row), B: N×K (ldb), both
  * dtype (bf16 or fp32), device; C: M×N fp32 (ldc), device.  lda and ldb must be
@@ -176,7 +239,7 @@ int dmuon_gemm_nt(const void* A, const void* B, float* C, int64_t M, int64_t N, 
  * each phase p < n the summed milliseconds ms[p] and the launch count count[p],
  * then clears the record.  Phases: 0 momentum + partial norms, 1 start (scale +
  * operand copies), 2 Gram, 3 square+poly, 4 apply, 5 update (k = 0 only),
- * 6 gemm_nt, 7 norm finalize. */
+ * 6 gemm_nt, 7 norm finalize, 8 adamw. */
 int dmuon_phase_timing(int32_t enable);
 int dmuon_phase_timing_read(double* ms, int64_t* count, int32_t n);
 

@@ -5,6 +5,7 @@ below only marshal arguments: momentum, normalisation, Newton–Schulz and the
 update all run in the library's HIP kernels on the caller's current stream.
 
     muon_step(grads, momenta, masters, lr=0.02, momentum=0.95, ...)
+    adamw_step(params, grads, exp_avgs, exp_avg_sqs, step=1, ...)  # the "adamw" route
     ns_batched(x, coeffs=(3.4445, -4.775, 2.0315), steps=5, ...)
     lpt_assign(rows, cols, batch, layer_id, n_slots, ...)   # host only
 """
@@ -15,7 +16,7 @@ import ctypes
 from . import _binding as _b
 from .workloads import HYPER  # noqa: F401
 
-__all__ = ["muon_step", "muon_step_workspace_size", "ns_batched", "lpt_assign", "gemm_nt",
+__all__ = ["muon_step", "muon_step_workspace_size", "adamw_step", "ns_batched", "lpt_assign", "gemm_nt",
            "phase_timing", "phase_timing_read", "abi_version", "load_library", "HYPER"]
 
 QUINTIC = (HYPER["a"], HYPER["b"], HYPER["c"])
@@ -43,16 +44,19 @@ def muon_step_workspace_size(grads, momenta, masters, *, steps=5, precision="bf1
 
 def muon_step(grads, momenta, masters, *, lr=HYPER["lr"], momentum=HYPER["mu"],
               weight_decay=HYPER["wd"], eps=HYPER["eps"], coeffs=QUINTIC, steps=HYPER["steps"],
-              precision="bf16", ns_outs=None, workspace=None, stream=None) -> None:
+              precision="bf16", grad_scale=1.0, ns_outs=None, param_outs=None, workspace=None,
+              stream=None) -> None:
     """One owner-rank Muon step over all given tensors, enqueued on ``stream``.
 
-    grads: bf16/fp32 GPU tensors (2-D or 3-D); momenta, masters: fp32, updated in
-    place; ns_outs: optional fp32 tensors that receive the Newton–Schulz output.
+    grads: bf16/fp32 GPU tensors (2-D or 3-D), read as grad_scale·grad; momenta,
+    masters: fp32, updated in place; ns_outs: optional fp32 tensors that receive
+    the Newton–Schulz output; param_outs: optional bf16 tensors that receive the
+    updated master rounded to bf16 (the published parameter).
     workspace: optional uint8 GPU tensor of at least ``muon_step_workspace_size``
     bytes (allocated here when omitted).
     """
-    cfg = _cfg(lr, momentum, weight_decay, eps, coeffs, steps, precision)
-    arr, n = _b.make_descs(grads, momenta, masters, ns_outs)
+    cfg = _b.make_cfg(lr, momentum, weight_decay, eps, coeffs, steps, precision, grad_scale)
+    arr, n = _b.make_descs(grads, momenta, masters, ns_outs, param_outs)
     if n == 0:
         return
     need = _b.muon_step_workspace_size(cfg, (arr, n))
@@ -62,6 +66,29 @@ def muon_step(grads, momenta, masters, *, lr=HYPER["lr"], momentum=HYPER["mu"],
     _b.check(L.dmuon_muon_step(arr, n, ctypes.byref(cfg), ctypes.c_void_p(workspace.data_ptr()),
                                workspace.numel() * workspace.element_size(),
                                _b._stream_handle(stream)))
+
+
+def adamw_step(params, grads, exp_avgs, exp_avg_sqs, *, step, lr=1e-3, betas=(0.9, 0.999),
+               eps=1e-8, weight_decay=0.01, grad_scale=1.0, param_outs=None, workspace=None,
+               stream=None) -> None:
+    """One AdamW step (the "adamw" route) over all given tensors in one launch.
+
+    params, exp_avgs, exp_avg_sqs: fp32 GPU tensors updated in place; grads: bf16
+    or fp32, read as grad_scale·grad; step ≥ 1 is the bias-correction step number;
+    param_outs: optional bf16 tensors that receive the updated parameter.
+    """
+    arr, n = _b.make_adamw_descs(params, grads, exp_avgs, exp_avg_sqs, param_outs)
+    if n == 0:
+        return
+    L = _b.lib()
+    need = ctypes.c_size_t(0)
+    _b.check(L.dmuon_adamw_step_workspace_size(arr, n, ctypes.byref(need)))
+    if workspace is None:
+        workspace = _b.alloc_workspace(need.value, params[0].device)
+    cfg = _b.AdamwCfg(lr, betas[0], betas[1], eps, weight_decay, grad_scale, int(step))
+    _b.check(L.dmuon_adamw_step(arr, n, ctypes.byref(cfg), ctypes.c_void_p(workspace.data_ptr()),
+                                workspace.numel() * workspace.element_size(),
+                                _b._stream_handle(stream)))
 
 
 def ns_batched(x, *, coeffs=QUINTIC, steps=HYPER["steps"], eps=HYPER["eps"], normalize=True,

@@ -27,10 +27,12 @@ ERRORS = {
 }
 F32, BF16 = 0, 1
 PREC = {"bf16": 0, "f32": 1}
-PHASES = ["momentum", "start", "gram", "square", "apply", "update", "gemm_nt", "norm"]
+PHASES = ["momentum", "start", "gram", "square", "apply", "update", "gemm_nt", "norm", "adamw"]
 EXPORTED = ["dmuon_muon_step_workspace_size", "dmuon_muon_step", "dmuon_ns_batched_workspace_size",
-            "dmuon_ns_batched", "dmuon_lpt_assign", "dmuon_gemm_nt", "dmuon_phase_timing",
-            "dmuon_phase_timing_read", "dmuon_last_error", "dmuon_abi_version"]
+            "dmuon_ns_batched", "dmuon_lpt_assign", "dmuon_adamw_step_workspace_size",
+            "dmuon_adamw_step", "dmuon_gemm_nt", "dmuon_phase_timing", "dmuon_phase_timing_read",
+            "dmuon_last_error", "dmuon_abi_version"]
+ABI_VERSION = 2
 
 
 class DmuonError(Exception):
@@ -41,14 +43,28 @@ class Tensor(ctypes.Structure):
     _fields_ = [("ndim", ctypes.c_int32), ("grad_dtype", ctypes.c_int32),
                 ("shape", ctypes.c_int64 * 3), ("grad", ctypes.c_void_p),
                 ("momentum", ctypes.c_void_p), ("master", ctypes.c_void_p),
-                ("ns_out", ctypes.c_void_p)]
+                ("ns_out", ctypes.c_void_p), ("param_out", ctypes.c_void_p)]
 
 
 class StepCfg(ctypes.Structure):
     _fields_ = [("lr", ctypes.c_float), ("momentum", ctypes.c_float),
                 ("weight_decay", ctypes.c_float), ("eps", ctypes.c_float),
                 ("a", ctypes.c_float), ("b", ctypes.c_float), ("c", ctypes.c_float),
-                ("ns_steps", ctypes.c_int32), ("prec", ctypes.c_int32)]
+                ("ns_steps", ctypes.c_int32), ("prec", ctypes.c_int32),
+                ("grad_scale", ctypes.c_float)]
+
+
+class AdamwTensor(ctypes.Structure):
+    _fields_ = [("numel", ctypes.c_int64), ("grad_dtype", ctypes.c_int32),
+                ("reserved", ctypes.c_int32), ("grad", ctypes.c_void_p),
+                ("param", ctypes.c_void_p), ("exp_avg", ctypes.c_void_p),
+                ("exp_avg_sq", ctypes.c_void_p), ("param_out", ctypes.c_void_p)]
+
+
+class AdamwCfg(ctypes.Structure):
+    _fields_ = [("lr", ctypes.c_float), ("beta1", ctypes.c_float), ("beta2", ctypes.c_float),
+                ("eps", ctypes.c_float), ("weight_decay", ctypes.c_float),
+                ("grad_scale", ctypes.c_float), ("step", ctypes.c_int32)]
 
 
 _lib = None
@@ -71,6 +87,8 @@ def lib():
     L.dmuon_ns_batched.argtypes = [vp, i32, vp, i64, i64, i64, f32, f32, f32, i32, f32, i32, i32,
                                    vp, sz, vp]
     L.dmuon_lpt_assign.argtypes = [i64, vp, vp, vp, vp, i32, i64, i32, vp, vp, i32, vp, vp, vp, vp]
+    L.dmuon_adamw_step_workspace_size.argtypes = [P(AdamwTensor), i32, P(sz)]
+    L.dmuon_adamw_step.argtypes = [P(AdamwTensor), i32, P(AdamwCfg), vp, sz, vp]
     L.dmuon_gemm_nt.argtypes = [vp, vp, vp, i64, i64, i64, i64, i64, i64, i32, vp]
     L.dmuon_phase_timing.argtypes = [i32]
     L.dmuon_phase_timing_read.argtypes = [vp, vp, i32]
@@ -79,8 +97,11 @@ def lib():
     L.dmuon_abi_version.restype = i32
     for name in ["dmuon_muon_step_workspace_size", "dmuon_muon_step",
                  "dmuon_ns_batched_workspace_size", "dmuon_ns_batched", "dmuon_lpt_assign",
+                 "dmuon_adamw_step_workspace_size", "dmuon_adamw_step",
                  "dmuon_gemm_nt", "dmuon_phase_timing", "dmuon_phase_timing_read"]:
         getattr(L, name).restype = ctypes.c_int
+    if L.dmuon_abi_version() != ABI_VERSION:
+        raise RuntimeError(f"{LIB_PATH} has ABI {L.dmuon_abi_version()}, expected {ABI_VERSION}: rebuild it")
     _lib = L
     return L
 
@@ -131,29 +152,45 @@ def _check_dev(t, what, dtype=None):
         raise ValueError(f"{what} must be {dtype}, got {t.dtype}")
 
 
-def make_cfg(lr, momentum, weight_decay, eps, coeffs, steps, precision) -> StepCfg:
+def make_cfg(lr, momentum, weight_decay, eps, coeffs, steps, precision, grad_scale=1.0) -> StepCfg:
     if precision not in PREC:
         raise ValueError(f"precision must be one of {sorted(PREC)}")
     a, b, c = coeffs
-    return StepCfg(lr, momentum, weight_decay, eps, a, b, c, int(steps), PREC[precision])
+    return StepCfg(lr, momentum, weight_decay, eps, a, b, c, int(steps), PREC[precision], grad_scale)
 
 
-def make_descs(grads, momenta, masters, ns_outs=None):
+def _bf16_words(t, what, shape):
+    """A bf16 (or int16/uint16 raw-word) GPU tensor of ``shape``: the published copy."""
+    torch = _torch()
+    _check_dev(t, what)
+    if t.dtype not in (torch.bfloat16, torch.int16, torch.uint16):
+        raise ValueError(f"{what} must hold bf16 words (bfloat16, int16 or uint16)")
+    if t.shape != shape:
+        raise ValueError(f"{what} must have shape {tuple(shape)}")
+
+
+def make_descs(grads, momenta, masters, ns_outs=None, param_outs=None):
     torch = _torch()
     n = len(grads)
     if not (len(momenta) == len(masters) == n):
         raise ValueError("grads, momenta and masters differ in length")
     if ns_outs is not None and len(ns_outs) != n:
         raise ValueError("ns_outs differs in length")
+    if param_outs is not None and len(param_outs) != n:
+        raise ValueError("param_outs differs in length")
     arr = (Tensor * max(n, 1))()
     for i in range(n):
         g, m, w = grads[i], momenta[i], masters[i]
         o = None if ns_outs is None else ns_outs[i]
+        q = None if param_outs is None else param_outs[i]
         _check_dev(g, f"grads[{i}]")
         _check_dev(m, f"momenta[{i}]", torch.float32)
         _check_dev(w, f"masters[{i}]", torch.float32)
         if o is not None:
             _check_dev(o, f"ns_outs[{i}]", torch.float32)
+        if q is not None:
+            _bf16_words(q, f"param_outs[{i}]", g.shape)
+        arr[i].param_out = None if q is None else q.data_ptr()
         if m.shape != g.shape or w.shape != g.shape or (o is not None and o.shape != g.shape):
             raise ValueError(f"tensor {i}: shapes of grad, momentum, master (and ns_out) differ")
         arr[i].ndim = g.dim()
@@ -164,6 +201,36 @@ def make_descs(grads, momenta, masters, ns_outs=None):
         arr[i].momentum = m.data_ptr()
         arr[i].master = w.data_ptr()
         arr[i].ns_out = None if o is None else o.data_ptr()
+    return arr, n
+
+
+def make_adamw_descs(params, grads, exp_avgs, exp_avg_sqs, param_outs=None):
+    torch = _torch()
+    n = len(params)
+    if not (len(grads) == len(exp_avgs) == len(exp_avg_sqs) == n):
+        raise ValueError("params, grads, exp_avgs and exp_avg_sqs differ in length")
+    if param_outs is not None and len(param_outs) != n:
+        raise ValueError("param_outs differs in length")
+    arr = (AdamwTensor * max(n, 1))()
+    for i in range(n):
+        p, g, m, v = params[i], grads[i], exp_avgs[i], exp_avg_sqs[i]
+        q = None if param_outs is None else param_outs[i]
+        _check_dev(p, f"params[{i}]", torch.float32)
+        _check_dev(g, f"grads[{i}]")
+        _check_dev(m, f"exp_avgs[{i}]", torch.float32)
+        _check_dev(v, f"exp_avg_sqs[{i}]", torch.float32)
+        if g.shape != p.shape or m.shape != p.shape or v.shape != p.shape:
+            raise ValueError(f"tensor {i}: shapes of param, grad, exp_avg, exp_avg_sq differ")
+        if q is not None:
+            _bf16_words(q, f"param_outs[{i}]", p.shape)
+        arr[i].numel = p.numel()
+        arr[i].grad_dtype = _dtype_code(g)
+        arr[i].reserved = 0
+        arr[i].grad = g.data_ptr()
+        arr[i].param = p.data_ptr()
+        arr[i].exp_avg = m.data_ptr()
+        arr[i].exp_avg_sq = v.data_ptr()
+        arr[i].param_out = None if q is None else q.data_ptr()
     return arr, n
 
 

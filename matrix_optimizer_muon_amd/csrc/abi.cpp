@@ -84,6 +84,7 @@ struct Item {
   float* mom;
   float* master;
   float* out;
+  uint16_t* pub;
 };
 
 struct Plan {
@@ -155,6 +156,7 @@ static int build_plan(const std::vector<Item>& items, int prec_f32, Plan& pl, ch
     P.mom = it.mom;
     P.master = it.master;
     P.out = it.out;
+    P.pub = it.pub;
     const int64_t b = it.batch;
     P.xf = (float*)carve((size_t)(b * it.rows * P.ld_x) * 4);
     P.xg = carve((size_t)(b * P.m * P.ld_n) * esz);
@@ -166,7 +168,7 @@ static int build_plan(const std::vector<Item>& items, int prec_f32, Plan& pl, ch
     P.part_apply = (float*)carve((size_t)(b * P.apply_tr * P.apply_tc) * 4);
     const int64_t tri = (int64_t)P.tiles_m * (P.tiles_m + 1) / 2;
     const int64_t cnt[PH_COUNT] = {b * P.chunks, b * P.prep_tiles_r * P.prep_tiles_c, b * tri, b * tri,
-                                   b * P.apply_tr * P.apply_tc, b * P.chunks, 0, b};
+                                   b * P.apply_tr * P.apply_tc, b * P.chunks, 0, b, 0};
     for (int ph = 0; ph < PH_COUNT; ++ph) {
       P.wg0[ph] = (int32_t)wg[ph];
       pl.prefix[(size_t)ph * (n + 1) + i] = (int32_t)wg[ph];
@@ -251,7 +253,7 @@ static int check_cfg(const dmuon_step_cfg* cfg) {
     return fail(DMUON_E_CFG, "ns_steps must be in [0, 64], got " + std::to_string(cfg->ns_steps));
   if (!finite(cfg->eps) || cfg->eps < 0.f) return fail(DMUON_E_CFG, "eps must be finite and >= 0");
   if (!finite(cfg->lr) || !finite(cfg->momentum) || !finite(cfg->weight_decay) || !finite(cfg->a) ||
-      !finite(cfg->b) || !finite(cfg->c))
+      !finite(cfg->b) || !finite(cfg->c) || !finite(cfg->grad_scale))
     return fail(DMUON_E_CFG, "hyper-parameters must be finite");
   return DMUON_OK;
 }
@@ -281,8 +283,10 @@ static int collect_items(const dmuon_tensor* t, int32_t n, std::vector<Item>& it
       rs->push_back({(uintptr_t)x.momentum, (uintptr_t)x.momentum + numel * 4, false});
       rs->push_back({(uintptr_t)x.master, (uintptr_t)x.master + numel * 4, false});
       if (x.ns_out) rs->push_back({(uintptr_t)x.ns_out, (uintptr_t)x.ns_out + numel * 4, false});
+      if (x.param_out) rs->push_back({(uintptr_t)x.param_out, (uintptr_t)x.param_out + numel * 2, false});
     }
-    items.push_back({batch, rows, cols, x.grad, x.grad_dtype == DMUON_BF16, x.momentum, x.master, x.ns_out});
+    items.push_back({batch, rows, cols, x.grad, x.grad_dtype == DMUON_BF16, x.momentum, x.master, x.ns_out,
+                     x.param_out});
   }
   return DMUON_OK;
 }
@@ -305,13 +309,91 @@ static int test_fail_hook() {
   return DMUON_OK;
 }
 
+// ---- the adamw route ------------------------------------------------------
+struct AdamwPlan {
+  std::vector<AdamwProblem> probs;
+  std::vector<int32_t> prefix;      // n + 1
+  int64_t total_wg = 0;
+  size_t off_prefix = 0, bytes = 0;
+};
+
+static int check_adamw_cfg(const dmuon_adamw_cfg* cfg) {
+  if (!cfg) return fail(DMUON_E_NULL, "cfg is NULL");
+  if (!finite(cfg->lr) || !finite(cfg->beta1) || !finite(cfg->beta2) || !finite(cfg->eps) ||
+      !finite(cfg->weight_decay) || !finite(cfg->grad_scale))
+    return fail(DMUON_E_CFG, "hyper-parameters must be finite");
+  if (cfg->lr < 0.f) return fail(DMUON_E_CFG, "lr must be >= 0");
+  if (cfg->beta1 < 0.f || cfg->beta1 >= 1.f || cfg->beta2 < 0.f || cfg->beta2 >= 1.f)
+    return fail(DMUON_E_CFG, "beta1 and beta2 must be in [0, 1)");
+  if (!(cfg->eps > 0.f)) return fail(DMUON_E_CFG, "eps must be > 0");
+  if (cfg->step < 1) return fail(DMUON_E_CFG, "step counts from 1");
+  return DMUON_OK;
+}
+
+static int collect_adamw(const dmuon_adamw_tensor* t, int32_t n, std::vector<const dmuon_adamw_tensor*>& items,
+                         std::vector<Range>* rs) {
+  if (n < 0) return fail(DMUON_E_SHAPE, "n_tensors < 0");
+  if (n > 0 && !t) return fail(DMUON_E_NULL, "tensors is NULL");
+  for (int32_t i = 0; i < n; ++i) {
+    const dmuon_adamw_tensor& x = t[i];
+    const std::string who = "tensor " + std::to_string(i) + ": ";
+    if (x.numel < 0) return fail(DMUON_E_SHAPE, who + "numel < 0");
+    if (x.numel > ((int64_t)1 << 40)) return fail(DMUON_E_SHAPE, who + "numel too large");
+    if (x.reserved != 0) return fail(DMUON_E_SHAPE, who + "reserved must be 0");
+    if (x.grad_dtype != DMUON_F32 && x.grad_dtype != DMUON_BF16)
+      return fail(DMUON_E_DTYPE, who + "grad_dtype must be DMUON_F32 or DMUON_BF16");
+    if (x.numel == 0) continue;
+    if (!x.grad || !x.param || !x.exp_avg || !x.exp_avg_sq)
+      return fail(DMUON_E_NULL, who + "grad, param, exp_avg and exp_avg_sq must be set");
+    if (rs) {
+      const size_t gs = x.grad_dtype == DMUON_BF16 ? 2 : 4;
+      const uintptr_t nb = (uintptr_t)x.numel;
+      rs->push_back({(uintptr_t)x.grad, (uintptr_t)x.grad + nb * gs, true});
+      rs->push_back({(uintptr_t)x.param, (uintptr_t)x.param + nb * 4, false});
+      rs->push_back({(uintptr_t)x.exp_avg, (uintptr_t)x.exp_avg + nb * 4, false});
+      rs->push_back({(uintptr_t)x.exp_avg_sq, (uintptr_t)x.exp_avg_sq + nb * 4, false});
+      if (x.param_out) rs->push_back({(uintptr_t)x.param_out, (uintptr_t)x.param_out + nb * 2, false});
+    }
+    items.push_back(&x);
+  }
+  return DMUON_OK;
+}
+
+static int build_adamw_plan(const std::vector<const dmuon_adamw_tensor*>& items, AdamwPlan& pl) {
+  const int n = (int)items.size();
+  pl.probs.assign(n, AdamwProblem{});
+  pl.prefix.assign(n + 1, 0);
+  int64_t wg = 0;
+  for (int i = 0; i < n; ++i) {
+    const dmuon_adamw_tensor& x = *items[i];
+    AdamwProblem& P = pl.probs[i];
+    P.numel = x.numel;
+    P.grad_bf16 = x.grad_dtype == DMUON_BF16;
+    P.chunks = (int32_t)cdiv(x.numel, kElemChunk);
+    P.wg0 = (int32_t)wg;
+    P.grad = x.grad;
+    P.param = x.param;
+    P.m = x.exp_avg;
+    P.v = x.exp_avg_sq;
+    P.pub = x.param_out;
+    pl.prefix[i] = (int32_t)wg;
+    wg += P.chunks;
+    if (wg > INT32_MAX) return fail(DMUON_E_SHAPE, "too many workgroups in one launch");
+  }
+  pl.prefix[n] = (int32_t)wg;
+  pl.total_wg = wg;
+  pl.off_prefix = align256((size_t)n * sizeof(AdamwProblem));
+  pl.bytes = n ? align256(pl.off_prefix + (size_t)(n + 1) * sizeof(int32_t)) : 0;
+  return DMUON_OK;
+}
+
 }  // namespace dmuon
 
 using namespace dmuon;
 
 extern "C" {
 
-int32_t dmuon_abi_version(void) { return 1; }
+int32_t dmuon_abi_version(void) { return 2; }
 
 const char* dmuon_last_error(void) { return g_err.c_str(); }
 
@@ -364,6 +446,7 @@ int dmuon_muon_step(const dmuon_tensor* tensors, int32_t n, const dmuon_step_cfg
   s.has_momentum = 1;
   s.normalize = 1;
   s.write_master = 1;
+  s.gscale = cfg->grad_scale;
   return run_plan(real, (char*)workspace, f32, s, cfg->ns_steps, stream);
 }
 
@@ -379,7 +462,7 @@ int dmuon_ns_batched_workspace_size(int64_t batch, int64_t rows, int64_t cols, i
     *bytes = 0;
     return DMUON_OK;
   }
-  std::vector<Item> items{{batch, rows, cols, nullptr, 0, nullptr, nullptr, nullptr}};
+  std::vector<Item> items{{batch, rows, cols, nullptr, 0, nullptr, nullptr, nullptr, nullptr}};
   Plan pl;
   int e = build_plan(items, prec == DMUON_PREC_F32, pl, nullptr);
   if (e) return e;
@@ -407,7 +490,7 @@ int dmuon_ns_batched(const void* x, int32_t x_dtype, float* out, int64_t batch, 
                         {(uintptr_t)out, (uintptr_t)out + numel * 4, false}};
   int e = check_alias(rs);
   if (e) return e;
-  std::vector<Item> items{{batch, rows, cols, x, x_dtype == DMUON_BF16, nullptr, nullptr, out}};
+  std::vector<Item> items{{batch, rows, cols, x, x_dtype == DMUON_BF16, nullptr, nullptr, out, nullptr}};
   const int f32 = prec == DMUON_PREC_F32;
   Plan pl;
   if ((e = build_plan(items, f32, pl, nullptr))) return e;
@@ -426,7 +509,67 @@ int dmuon_ns_batched(const void* x, int32_t x_dtype, float* out, int64_t batch, 
   s.has_momentum = 0;
   s.normalize = normalize;
   s.write_master = 0;
+  s.gscale = 1.f;
   return run_plan(real, (char*)workspace, f32, s, steps, stream);
+}
+
+int dmuon_adamw_step_workspace_size(const dmuon_adamw_tensor* tensors, int32_t n, size_t* bytes) {
+  g_err.clear();
+  if (!bytes) return fail(DMUON_E_NULL, "bytes is NULL");
+  std::vector<const dmuon_adamw_tensor*> items;
+  int e = collect_adamw(tensors, n, items, nullptr);
+  if (e) return e;
+  AdamwPlan pl;
+  if ((e = build_adamw_plan(items, pl))) return e;
+  *bytes = pl.bytes;
+  return DMUON_OK;
+}
+
+int dmuon_adamw_step(const dmuon_adamw_tensor* tensors, int32_t n, const dmuon_adamw_cfg* cfg, void* workspace,
+                     size_t workspace_bytes, void* stream) {
+  g_err.clear();
+  int e = check_adamw_cfg(cfg);
+  if (e) return e;
+  std::vector<const dmuon_adamw_tensor*> items;
+  std::vector<Range> rs;
+  if ((e = collect_adamw(tensors, n, items, &rs))) return e;
+  if (items.empty()) return DMUON_OK;
+  if ((e = check_alias(rs))) return e;
+  AdamwPlan pl;
+  if ((e = build_adamw_plan(items, pl))) return e;
+  if ((e = check_workspace(workspace, workspace_bytes, pl.bytes))) return e;
+  const uintptr_t wlo = (uintptr_t)workspace, whi = wlo + pl.bytes;
+  for (const Range& r : rs)
+    if (r.lo < whi && wlo < r.hi) return fail(DMUON_E_ALIAS, "workspace overlaps a tensor buffer");
+  if ((e = test_fail_hook())) return e;
+  std::vector<char> host(pl.bytes, 0);
+  std::memcpy(host.data(), pl.probs.data(), pl.probs.size() * sizeof(AdamwProblem));
+  std::memcpy(host.data() + pl.off_prefix, pl.prefix.data(), pl.prefix.size() * sizeof(int32_t));
+  char* ws = (char*)workspace;
+  e = upload_async(ws, host.data(), host.size(), stream);
+  if (e) return fail(DMUON_E_HIP, std::string("table upload: ") + hip_error_string(e));
+  // bias corrections in double on the host (step is exact as an integer)
+  const double b1 = cfg->beta1, b2 = cfg->beta2;
+  const double bc1 = 1.0 - std::pow(b1, (double)cfg->step);
+  const double bc2 = 1.0 - std::pow(b2, (double)cfg->step);
+  AdamwScalars s{};
+  s.decay = (float)(1.0 - (double)cfg->lr * (double)cfg->weight_decay);
+  s.step_size = (float)((double)cfg->lr / bc1);
+  s.inv_sqrt_bc2 = (float)(1.0 / std::sqrt(bc2));
+  s.eps = cfg->eps;
+  s.beta1 = cfg->beta1;
+  s.one_m_beta1 = (float)(1.0 - b1);
+  s.beta2 = cfg->beta2;
+  s.one_m_beta2 = (float)(1.0 - b2);
+  s.gscale = cfg->grad_scale;
+  AdamwTable tab;
+  tab.probs = (const AdamwProblem*)ws;
+  tab.wg_prefix = (const int32_t*)(ws + pl.off_prefix);
+  tab.n_probs = (int32_t)pl.probs.size();
+  tab.total_wg = (int32_t)pl.total_wg;
+  const int r = launch_adamw(tab, s, stream);
+  if (r) return fail(DMUON_E_HIP, std::string("launch failed: ") + hip_error_string(r));
+  return DMUON_OK;
 }
 
 int dmuon_gemm_nt(const void* A, const void* B, float* C, int64_t M, int64_t N, int64_t K, int64_t lda, int64_t ldb,

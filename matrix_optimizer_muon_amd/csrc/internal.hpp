@@ -26,7 +26,8 @@ enum Phase : int {
   PH_UPDATE = 5,     // W ← (1 − lr wd) W − lr X0 (only when k = 0)
   PH_GEMM = 6,       // test hook: plain NT product
   PH_NORM = 7,       // per-slice norm finalize: inv = 1/(‖B‖_F + eps), d₀
-  PH_COUNT = 8
+  PH_ADAMW = 8,      // the adamw route (its own launch table)
+  PH_COUNT = 9
 };
 
 // One tensor (2-D = batch 1, or 3-D batch of slices) as the kernels see it.
@@ -53,6 +54,7 @@ struct DevProblem {
   float* mom;                  // momentum (NULL for ns_batched)
   float* master;               // master weight (NULL for ns_batched)
   float* out;                  // NS output (NULL if not wanted)
+  uint16_t* pub;               // bf16 published parameter (NULL if not wanted)
   // workspace (operand element type = bf16 or fp32 per precision)
   float* xf;                   // fp32 iterate, storage layout rows×ld_x, stride rows*ld_x
   void* xg;                    // oriented X, m×ld_n, stride m*ld_n
@@ -73,6 +75,7 @@ struct LaunchScalars {
   int32_t has_momentum;        // 0 for ns_batched
   int32_t normalize;
   int32_t write_master;
+  float gscale;                // gradient-ingest scale s (B ← μB + s·G)
 };
 
 struct LaunchTable {
@@ -83,11 +86,42 @@ struct LaunchTable {
   int32_t total_wg;            // workgroups of this launch
 };
 
+// ---- the adamw route ----------------------------------------------------
+struct AdamwProblem {
+  int64_t numel;
+  int32_t grad_bf16;
+  int32_t chunks;              // workgroups (kElemChunk elements each)
+  int32_t wg0;                 // first workgroup of this tensor
+  int32_t pad;
+  const void* grad;
+  float* param;
+  float* m;
+  float* v;
+  uint16_t* pub;
+};
+
+struct AdamwScalars {
+  float decay;                 // 1 − lr·wd
+  float step_size;             // lr / (1 − β₁ᵗ)
+  float inv_sqrt_bc2;          // 1 / √(1 − β₂ᵗ)
+  float eps;
+  float beta1, one_m_beta1, beta2, one_m_beta2;
+  float gscale;
+};
+
+struct AdamwTable {
+  const AdamwProblem* probs;   // device
+  const int32_t* wg_prefix;    // device, [n_probs + 1]
+  int32_t n_probs;
+  int32_t total_wg;
+};
+
 // Kernel launchers (kernels.hip).  Return 0 or a hipError_t value.
 int launch_phase(int phase, int prec_f32, const LaunchTable& tab, const LaunchScalars& s,
                  void* stream);
 int launch_gemm_nt(const void* A, const void* B, float* C, int64_t M, int64_t N, int64_t K,
                    int64_t lda, int64_t ldb, int64_t ldc, int f32, void* stream);
+int launch_adamw(const AdamwTable& tab, const AdamwScalars& s, void* stream);
 const char* hip_error_string(int err);
 int upload_async(void* dst, const void* src, size_t bytes, void* stream);
 

@@ -34,6 +34,7 @@ namespace dmuon {
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef unsigned u32x4_t __attribute__((ext_vector_type(4)));
 
 // Global-memory (address space 1) view of a pointer.  Pointers read out of the
 // device-side problem table are generic to the compiler, which would otherwise
@@ -138,6 +139,8 @@ __global__ __launch_bounds__(kThreads) void k_momentum(LaunchTable tab, LaunchSc
         x[4] = v.x; x[5] = v.y; x[6] = v.z; x[7] = v.w;
       }
       if (mom) {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) x[i] *= s.gscale;
         float4 u = *(const float4*)(mom + e), v = *(const float4*)(mom + e + 4);
         u.x = fmaf(mu, u.x, x[0]); u.y = fmaf(mu, u.y, x[1]);
         u.z = fmaf(mu, u.z, x[2]); u.w = fmaf(mu, u.w, x[3]);
@@ -158,7 +161,7 @@ __global__ __launch_bounds__(kThreads) void k_momentum(LaunchTable tab, LaunchSc
   for (int64_t e = done + threadIdx.x; e < e1; e += kThreads) {
     float x = P.grad_bf16 ? bf16_to_f32(gb[e]) : gf[e];
     if (mom) {
-      x = fmaf(mu, mom[e], x);
+      x = fmaf(mu, mom[e], s.gscale * x);
       mom[e] = x;
     }
     acc = fmaf(x, x, acc);
@@ -330,7 +333,102 @@ __global__ __launch_bounds__(kThreads) void k_update(LaunchTable tab, LaunchScal
     const int64_t r = e / P.cols, c = e - r * P.cols;
     const float x = xf[r * P.ld_x + c];
     if (P.out) P.out[base + e] = x;
-    if (s.write_master) P.master[base + e] = fmaf(-s.lr, x, s.decay * P.master[base + e]);
+    if (s.write_master) {
+      const float w = fmaf(-s.lr, x, s.decay * P.master[base + e]);
+      P.master[base + e] = w;
+      if (P.pub) P.pub[base + e] = f32_to_bf16(w);
+    }
+  }
+}
+
+// bf16 pair (lo, hi) packed into one dword, round to nearest even
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  const f32x2_t v = {lo, hi};
+  const bf16x2_t b = __builtin_convertvector(v, bf16x2_t);
+  uint32_t u;
+  __builtin_memcpy(&u, &b, 4);
+  return u;
+}
+// ---------------------------------------------------------------------------
+// the adamw route: one AdamW step per element over a grouped list of tensors
+// (routing page, route table: the owner runs AdamW on small and 1-D parameters;
+// the steps are the published AdamW: decoupled decay, bias-corrected moments)
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ void adamw_elem(float& p, float& m, float& v, float g, const AdamwScalars& s) {
+  g *= s.gscale;
+  p *= s.decay;
+  m = fmaf(s.beta1, m, s.one_m_beta1 * g);
+  v = fmaf(s.beta2, v, s.one_m_beta2 * g * g);
+  const float denom = sqrtf(v) * s.inv_sqrt_bc2 + s.eps;   // √v̂ + eps
+  p = p - s.step_size * (m / denom);                        // lr·m̂ / (√v̂ + eps)
+}
+
+__global__ __launch_bounds__(kThreads) void k_adamw(AdamwTable tab, AdamwScalars s) {
+  const int bid = blockIdx.x;
+  const AdamwProblem& P = tab.probs[find_prob(tab.wg_prefix, tab.n_probs, bid)];
+  const int64_t e0 = (int64_t)(bid - P.wg0) * kElemChunk;
+  const int64_t e1 = (e0 + kElemChunk < P.numel) ? e0 + kElemChunk : P.numel;
+  const gptr<float> pp = glob(P.param);
+  const gptr<float> mm = glob(P.m);
+  const gptr<float> vv = glob(P.v);
+  const gptr<uint16_t> pub = P.pub ? glob(P.pub) : nullptr;
+  const gptr<const uint16_t> gb = glob((const uint16_t*)P.grad);
+  const gptr<const float> gf = glob((const float*)P.grad);
+  const bool aligned = (((uintptr_t)(P.param + e0) | (uintptr_t)(P.m + e0) | (uintptr_t)(P.v + e0)) & 15) == 0 &&
+                       (P.grad_bf16 ? ((uintptr_t)((const uint16_t*)P.grad + e0) & 15) == 0
+                                    : ((uintptr_t)((const float*)P.grad + e0) & 15) == 0) &&
+                       (!P.pub || ((uintptr_t)(P.pub + e0) & 15) == 0);
+  int64_t done = e0;
+  if (aligned) {
+    const int64_t nvec = (e1 - e0) >> 3;
+    for (int64_t q = threadIdx.x; q < nvec; q += kThreads) {
+      const int64_t e = e0 + q * 8;
+      float g[8];
+      if (P.grad_bf16) {
+        const u32x4_t raw = *(const gptr<const u32x4_t>)(gb + e);
+        const uint32_t w[4] = {raw.x, raw.y, raw.z, raw.w};
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          g[2 * k] = __uint_as_float(w[k] << 16);
+          g[2 * k + 1] = __uint_as_float(w[k] & 0xffff0000u);
+        }
+      } else {
+        const f32x4_t a = *(const gptr<const f32x4_t>)(gf + e), b = *(const gptr<const f32x4_t>)(gf + e + 4);
+        g[0] = a.x; g[1] = a.y; g[2] = a.z; g[3] = a.w; g[4] = b.x; g[5] = b.y; g[6] = b.z; g[7] = b.w;
+      }
+      f32x4_t p4[2], m4[2], v4[2];
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        p4[h] = *(const gptr<const f32x4_t>)(pp + e + 4 * h);
+        m4[h] = *(const gptr<const f32x4_t>)(mm + e + 4 * h);
+        v4[h] = *(const gptr<const f32x4_t>)(vv + e + 4 * h);
+      }
+      float pv[8] = {p4[0].x, p4[0].y, p4[0].z, p4[0].w, p4[1].x, p4[1].y, p4[1].z, p4[1].w};
+      float mv[8] = {m4[0].x, m4[0].y, m4[0].z, m4[0].w, m4[1].x, m4[1].y, m4[1].z, m4[1].w};
+      float vv8[8] = {v4[0].x, v4[0].y, v4[0].z, v4[0].w, v4[1].x, v4[1].y, v4[1].z, v4[1].w};
+#pragma unroll
+      for (int k = 0; k < 8; ++k) adamw_elem(pv[k], mv[k], vv8[k], g[k], s);
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        *(gptr<f32x4_t>)(pp + e + 4 * h) = f32x4_t{pv[4 * h], pv[4 * h + 1], pv[4 * h + 2], pv[4 * h + 3]};
+        *(gptr<f32x4_t>)(mm + e + 4 * h) = f32x4_t{mv[4 * h], mv[4 * h + 1], mv[4 * h + 2], mv[4 * h + 3]};
+        *(gptr<f32x4_t>)(vv + e + 4 * h) = f32x4_t{vv8[4 * h], vv8[4 * h + 1], vv8[4 * h + 2], vv8[4 * h + 3]};
+      }
+      if (pub)
+        *(gptr<u32x4_t>)(pub + e) = u32x4_t{pack_bf16x2(pv[0], pv[1]), pack_bf16x2(pv[2], pv[3]),
+                                            pack_bf16x2(pv[4], pv[5]), pack_bf16x2(pv[6], pv[7])};
+    }
+    done = e0 + nvec * 8;
+  }
+  for (int64_t e = done + threadIdx.x; e < e1; e += kThreads) {
+    float p = pp[e], m = mm[e], v = vv[e];
+    adamw_elem(p, m, v, P.grad_bf16 ? bf16_to_f32(gb[e]) : gf[e], s);
+    pp[e] = p;
+    mm[e] = m;
+    vv[e] = v;
+    if (pub) pub[e] = f32_to_bf16(p);
   }
 }
 
@@ -361,8 +459,6 @@ constexpr int kStages = 4;
 constexpr int kGemmLds = kStages * kStageBytes;        // 128 KiB
 constexpr int kDmaPerStage = 4;                        // buffer_load … lds per thread per stage
 static_assert(kTile == 256 && kGemmWaves == 8, "fragment layout assumes 8 waves on a 256 tile");
-
-typedef unsigned u32x4_t __attribute__((ext_vector_type(4)));
 
 struct Operands {
   const char* a;     // first A row of the tile
@@ -656,16 +752,6 @@ __device__ __forceinline__ void sym_epilogue(const DevProblem& P, const LaunchSc
   }
 }
 
-// bf16 pair (lo, hi) packed into one dword, round to nearest even
-typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
-typedef float f32x2_t __attribute__((ext_vector_type(2)));
-__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
-  const f32x2_t v = {lo, hi};
-  const bf16x2_t b = __builtin_convertvector(v, bf16x2_t);
-  uint32_t u;
-  __builtin_memcpy(&u, &b, 4);
-  return u;
-}
 // value of the neighbouring lane (lane ^ 1)
 __device__ __forceinline__ float swap_adjacent(float x) {
   return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0xB1, 0xF, 0xF, false));
@@ -737,16 +823,26 @@ __device__ __forceinline__ void apply_epilogue(const DevProblem& P, const Launch
   for (int j = 0; j < 2; ++j)
     xo[j] = lc0 + 32 * j < tcols ? (lr0 * ldx + (unsigned)(col0 + lc0 + 32 * j)) * 4u : kOob;
 
-  __amdgpu_buffer_rsrc_t rw = rx, ro = rx, rd = rx, rt = rx;
-  unsigned wo[2] = {0, 0}, dofs[2] = {0, 0}, tofs[2] = {0, 0};
+  __amdgpu_buffer_rsrc_t rw = rx, ro = rx, rd = rx, rt = rx, rp = rx;
+  unsigned wo[2] = {0, 0}, dofs[2] = {0, 0}, tofs[2] = {0, 0}, po[2] = {0, 0};
   unsigned ld_s = 0, ld_t = 0;
+  // published bf16 copy: two columns per dword when rows hold an even number of
+  // columns (a pair never straddles rows), else one 16-bit store per element
+  const bool pub_pairs = (cols & 1) == 0;
   if (LAST) {
     const int64_t first = ((int64_t)slice * rows + row0) * cols, bytes = (int64_t)trows * cols * 4;
     rw = range_rsrc(s.write_master ? P.master + first : nullptr, bytes);
     ro = range_rsrc(P.out ? P.out + first : nullptr, bytes);
+    rp = range_rsrc(s.write_master && P.pub ? P.pub + first : nullptr, (int64_t)trows * cols * 2);
 #pragma unroll
-    for (int j = 0; j < 2; ++j)
+    for (int j = 0; j < 2; ++j) {
       wo[j] = lc0 + 32 * j < tcols ? (lr0 * (unsigned)cols + (unsigned)(col0 + lc0 + 32 * j)) * 4u : kOob;
+      const unsigned gc = (unsigned)(col0 + lc0 + 32 * j);
+      po[j] = lc0 + 32 * j < tcols
+                  ? (pub_pairs ? ((lr0 + (odd ? 1u : 0u)) * (unsigned)cols + (gc & ~1u)) * 2u
+                               : (lr0 * (unsigned)cols + gc) * 2u)
+                  : kOob;
+    }
   } else {
     ld_s = (unsigned)(P.wide ? P.ld_n : P.ld_m);
     ld_t = (unsigned)(P.wide ? P.ld_m : P.ld_n);
@@ -789,12 +885,31 @@ __device__ __forceinline__ void apply_epilogue(const DevProblem& P, const Launch
 #pragma unroll
     for (int r = 0; r < 16; ++r) v[r] = fmaf(alpha, xin[slot][r], acc[i][j][r]);
     if (LAST) {
+      float w[16];
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const unsigned rr = (unsigned)(32 * i + 8 * (r >> 2) + (r & 3));
         const unsigned o = wo[j] + rr * (unsigned)cols * 4u;
+        w[r] = fmaf(-s.lr, v[r], s.decay * win[LAST ? slot : 0][r]);
         buf_st(ro, o, v[r]);
-        buf_st(rw, o, fmaf(-s.lr, v[r], s.decay * win[LAST ? slot : 0][r]));
+        buf_st(rw, o, w[r]);
+      }
+      if (pub_pairs) {
+#pragma unroll
+        for (int rq = 0; rq < 4; ++rq)
+#pragma unroll
+          for (int pe = 0; pe < 2; ++pe) {
+            const float w0 = w[4 * rq + 2 * pe], w1 = w[4 * rq + 2 * pe + 1];
+            const float got = swap_adjacent(odd ? w0 : w1);
+            const unsigned rr = (unsigned)(32 * i + 8 * rq + 2 * pe);
+            buf_st(rp, po[j] + rr * (unsigned)cols * 2u, odd ? pack_bf16x2(got, w1) : pack_bf16x2(w0, got));
+          }
+      } else {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const unsigned rr = (unsigned)(32 * i + 8 * (r >> 2) + (r & 3));
+          __builtin_amdgcn_raw_buffer_store_b16(f32_to_bf16(w[r]), rp, (int)(po[j] + rr * (unsigned)cols * 2u), 0, 0);
+        }
       }
     } else {
 #pragma unroll
@@ -984,6 +1099,15 @@ static int ensure_lds(int f32) {
     e |= set_lds(k_gemm_plain<uint16_t>);
   }
   if (e == 0) flag = 1;
+  return e;
+}
+
+int launch_adamw(const AdamwTable& tab, const AdamwScalars& s, void* stream) {
+  if (tab.total_wg <= 0) return 0;
+  timing_before(PH_ADAMW, stream);
+  hipLaunchKernelGGL(k_adamw, dim3(tab.total_wg), dim3(kThreads), 0, (hipStream_t)stream, tab, s);
+  const int e = (int)hipGetLastError();
+  timing_after(PH_ADAMW, stream);
   return e;
 }
 

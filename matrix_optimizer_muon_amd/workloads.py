@@ -29,6 +29,16 @@ Workloads (shapes are rows × cols of each gradient matrix):
   decaying spectrum.
 * ``mlp_moe_large``: 4 matrices 8192×28672 and one expert tensor
   [64, 1408, 2048]; bf16 N(0, 1e-3²).
+
+Inputs of the ``adamw`` route (1-D parameters; role 0 = gradient, 1 = parameter,
+4 = first moment, 5 = second moment):
+* ``adamw_llama_norms``: the 65 RMSNorm weight vectors of the 32-layer d = 4096
+  model (two per layer and the final norm), 4096 elements each, bf16
+  N(0, 1e-3²) gradients, parameters 1 + N(0, 0.02²);
+* ``adamw_stream``: 16 vectors of 4 Mi elements with the same draws, a size at
+  which the step is bound by HBM bandwidth.
+The optimizer state is drawn as m ~ N(0, 1e-4²) and v = (N(0, 1e-3²))² (a
+valid, non-negative second moment), or zero for a fresh state.
 """
 from __future__ import annotations
 
@@ -48,6 +58,8 @@ WORKLOAD_IDS = {
     "llama_d4096": 2,
     "merged_small": 3,
     "mlp_moe_large": 4,
+    "adamw_llama_norms": 5,
+    "adamw_stream": 6,
 }
 
 
@@ -106,6 +118,17 @@ def workload(name: str) -> Workload:
         for i in range(4):
             wl.tensors.append(TensorSpec(i, f"mlp.{i}", (8192, 28672), "bf16", "gauss", 1e-3))
         wl.tensors.append(TensorSpec(4, "experts", (64, 1408, 2048), "bf16", "gauss", 1e-3))
+        return wl
+    if name == "adamw_llama_norms":
+        wl = Workload(name, wid)
+        names = [f"layers.{lay}.{n}" for lay in range(32) for n in ("input_norm", "post_attn_norm")]
+        for i, nm in enumerate(names + ["final_norm"]):
+            wl.tensors.append(TensorSpec(i, nm, (4096,), "bf16", "norm", 1e-3, i // 2))
+        return wl
+    if name == "adamw_stream":
+        wl = Workload(name, wid)
+        for i in range(16):
+            wl.tensors.append(TensorSpec(i, f"vec.{i}", (4 << 20,), "bf16", "norm", 1e-3))
         return wl
     raise KeyError(name)
 
@@ -194,3 +217,40 @@ def make_custom(shape, grad_dtype="f32", seed=(99, 0), scale=1.0, nonzero_moment
     spec = TensorSpec(seed[1], "custom", tuple(shape), grad_dtype, kind, scale)
     wl = Workload("custom", seed[0], [spec])
     return make_tensor(wl, spec, nonzero_momentum=nonzero_momentum)
+
+
+@dataclass
+class AdamwData:
+    """Host arrays of one ``adamw``-route parameter (fp32; bf16 gradients as in TensorData)."""
+    spec: TensorSpec
+    grad: np.ndarray
+    grad_bits: np.ndarray | None
+    param: np.ndarray
+    exp_avg: np.ndarray
+    exp_avg_sq: np.ndarray
+
+
+def make_adamw(wl: Workload, spec: TensorSpec, fresh_state=False) -> AdamwData:
+    shape = spec.shape
+    g = gaussian(shape, spec.scale, rng_for(wl.wid, spec.index, 0))
+    bits = None
+    if spec.grad_dtype == "bf16":
+        bits = f32_to_bf16_bits(g)
+        g = bf16_bits_to_f32(bits).reshape(shape)
+    p = gaussian(shape, 0.02, rng_for(wl.wid, spec.index, 1))
+    if spec.kind == "norm":
+        p = p + np.float32(1.0)
+    if fresh_state:
+        m = np.zeros(shape, dtype=np.float32)
+        v = np.zeros(shape, dtype=np.float32)
+    else:
+        m = gaussian(shape, 1e-4, rng_for(wl.wid, spec.index, 4))
+        r = gaussian(shape, 1e-3, rng_for(wl.wid, spec.index, 5))
+        v = r * r
+    return AdamwData(spec, g, None if bits is None else bits.reshape(shape), p, m, v)
+
+
+def make_adamw_custom(numel, grad_dtype="f32", seed=(98, 0), scale=1e-3, fresh_state=False) -> AdamwData:
+    """A single ``adamw``-route parameter of ``numel`` elements for parity tests."""
+    spec = TensorSpec(seed[1], "custom", (int(numel),), grad_dtype, "norm", scale)
+    return make_adamw(Workload("custom", seed[0], [spec]), spec, fresh_state=fresh_state)

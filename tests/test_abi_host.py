@@ -32,7 +32,7 @@ def test_library_exports_every_header_function():
     for name in names:
         assert hasattr(L, name), name
     assert sorted(B.EXPORTED) == names
-    assert L.dmuon_abi_version() == 1
+    assert L.dmuon_abi_version() == 2 == B.ABI_VERSION
 
 
 # --------------------------------------------------------------------------
@@ -103,6 +103,7 @@ def desc(ndim=2, shape=(8, 16), dtype=B.F32, base=FAKE, numel_bytes=1 << 20):
     t.momentum = base + numel_bytes
     t.master = base + 2 * numel_bytes
     t.ns_out = None
+    t.param_out = None
     return t
 
 
@@ -146,6 +147,9 @@ def test_rejects_bad_arguments():
     assert step([desc()], cfg(steps=-1)) == -5
     assert step([desc()], cfg(eps=-1.0)) == -5
     assert step([desc()], cfg(lr=float("nan"))) == -5
+    c = cfg()
+    c.grad_scale = float("inf")
+    assert step([desc()], c) == -5
     bad = desc()
     bad.master = None
     assert step([bad]) == -1
@@ -174,6 +178,17 @@ def test_rejects_aliasing():
     assert rc == 0 and need > 0
     # workspace overlapping a tensor
     assert step([desc()], ws=FAKE, ws_bytes=1 << 40) == -7
+    # the published copy is a written buffer: it may not cover the gradient or the master
+    a = desc()
+    a.param_out = a.grad
+    assert step([a]) == -7
+    a = desc()
+    a.param_out = a.master + 64
+    assert step([a]) == -7
+    a = desc()
+    a.param_out = FAKE + (3 << 20)
+    rc, need = wsize([a])
+    assert rc == 0 and need > 0
 
 
 def test_zero_size_is_noop_and_needs_no_workspace():
@@ -230,3 +245,85 @@ def test_python_wrappers_raise_value_error():
         B.check(-2)
     with pytest.raises(RuntimeError):
         B.check(-8)
+
+
+# --------------------------------------------------------------------------
+# the adamw route
+# --------------------------------------------------------------------------
+def adesc(numel=1000, dtype=B.F32, base=FAKE, span=1 << 20):
+    t = B.AdamwTensor()
+    t.numel = numel
+    t.grad_dtype = dtype
+    t.reserved = 0
+    t.grad = base
+    t.param = base + span
+    t.exp_avg = base + 2 * span
+    t.exp_avg_sq = base + 3 * span
+    t.param_out = None
+    return t
+
+
+def acfg(**kw):
+    c = dict(lr=1e-3, beta1=0.9, beta2=0.999, eps=1e-8, weight_decay=0.01, grad_scale=1.0, step=1)
+    c.update(kw)
+    return B.AdamwCfg(c["lr"], c["beta1"], c["beta2"], c["eps"], c["weight_decay"], c["grad_scale"],
+                      c["step"])
+
+
+def astep(descs, c=None, ws=FAKE + (1 << 40), ws_bytes=1 << 40):
+    arr = (B.AdamwTensor * max(len(descs), 1))(*descs)
+    return B.lib().dmuon_adamw_step(arr, len(descs), ctypes.byref(c or acfg()), ctypes.c_void_p(ws),
+                                    ws_bytes, None)
+
+
+def awsize(descs):
+    arr = (B.AdamwTensor * max(len(descs), 1))(*descs)
+    out = ctypes.c_size_t(0)
+    rc = B.lib().dmuon_adamw_step_workspace_size(arr, len(descs), ctypes.byref(out))
+    return rc, out.value
+
+
+def test_adamw_validation():
+    assert astep([adesc(numel=-1)]) == -3
+    assert astep([adesc(dtype=9)]) == -4
+    bad = adesc()
+    bad.reserved = 1
+    assert astep([bad]) == -3
+    bad = adesc()
+    bad.exp_avg_sq = None
+    assert astep([bad]) == -1
+    assert astep([adesc()], acfg(step=0)) == -5
+    assert astep([adesc()], acfg(beta1=1.0)) == -5
+    assert astep([adesc()], acfg(beta2=-0.1)) == -5
+    assert astep([adesc()], acfg(eps=0.0)) == -5
+    assert astep([adesc()], acfg(lr=-1.0)) == -5
+    assert astep([adesc()], acfg(grad_scale=float("nan"))) == -5
+    assert astep([adesc()], ws=0) == -6
+    assert astep([adesc()], ws_bytes=8) == -6
+    arr = (B.AdamwTensor * 1)()
+    assert B.lib().dmuon_adamw_step(arr, 1, None, None, 0, None) == -1
+    assert B.lib().dmuon_adamw_step(None, 1, ctypes.byref(acfg()), None, 0, None) == -1
+
+
+def test_adamw_aliasing_and_sizes():
+    a = adesc()
+    a.exp_avg = a.param                       # written twice
+    assert astep([a]) == -7
+    a = adesc()
+    a.param_out = a.grad
+    assert astep([a]) == -7
+    x, y = adesc(base=FAKE), adesc(base=FAKE + (1 << 20))   # y.grad == x.param
+    assert astep([x, y]) == -7
+    assert astep([adesc()], ws=FAKE, ws_bytes=1 << 40) == -7
+    assert astep([adesc(numel=0)], ws=0, ws_bytes=0) == 0
+    assert astep([], ws=0, ws_bytes=0) == 0
+    assert awsize([adesc(numel=0)]) == (0, 0)
+    rc1, s1 = awsize([adesc()])
+    rc2, s2 = awsize([adesc(base=FAKE + (i << 24)) for i in range(40)])
+    assert rc1 == rc2 == 0 and 0 < s1 < s2
+
+
+def test_adamw_forced_failure(monkeypatch):
+    monkeypatch.setenv("DMUON_TEST_FAIL_AT", "plan")
+    assert astep([adesc()]) == -8
+    monkeypatch.delenv("DMUON_TEST_FAIL_AT")
