@@ -1,6 +1,7 @@
 """Throughput of the owner-rank Muon step on one MI355X.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--publish]
+    python bench.py --route adamw [--workload adamw_stream|adamw_llama_norms]
 
 A step is one call of ``dmuon_muon_step`` over every matrix of the workload
 (momentum, per-slice normalisation, k = 5 quintic Newton–Schulz iterations,
@@ -9,7 +10,13 @@ Prints one JSON line.  ``value`` is matrices stepped per second; the line also
 carries the effective TFLOP/s (Σ k·(4m²n + 2m³) per step), its share of the bf16
 dense matrix-core peak, a roofline entry for the dominant kernel (timed with HIP
 events on the launch stream during the timed steps) and the fp64 CPU oracle
-timed on a bounded sample of the same workload.
+timed on a bounded sample of the same workload.  ``--publish`` also writes the
+bf16 published copy of every updated master inside the step.
+
+``--route adamw`` measures the ``adamw`` route instead: one ``dmuon_adamw_step``
+over the workload's 1-D parameters per step; ``value`` is elements per second
+and the roofline is HBM bandwidth against algorithmic bytes (gradient read,
+parameter and both moments read and written, plus the bf16 copy).
 """
 from __future__ import annotations
 
@@ -26,6 +33,8 @@ PEAK_BF16_TFLOPS = 2500.0     # MI355X dense bf16 matrix-core peak (published)
 PEAK_HBM_GBS = 8000.0         # MI355X HBM3E (published)
 DEFAULT_WORKLOAD = "layer_d2048"
 METRIC = "Muon NS step matrices/s + TFLOP/s and % bf16 MFMA peak, 1\u00d7MI355X"
+ADAMW_METRIC = "adamw route elements/s (owner 1-D parameters), 1\u00d7MI355X"
+ADAMW_DEFAULT_WORKLOAD = "adamw_stream"
 KERNELS_SRC = os.path.join(ROOT, "matrix_optimizer_muon_amd", "csrc", "kernels.hip")
 PROFILES = os.path.join(ROOT, "profiles")
 
@@ -153,6 +162,106 @@ def cpu_baseline(wl, ts, budget_s=20.0):
             "seconds": total, "gflops_fp64": ns_flops(chosen, HYPER["steps"]) / total / 1e9}
 
 
+def adamw_bytes_per_elem(grad_dtype, publish):
+    """Algorithmic HBM bytes per element of one AdamW step."""
+    return (2 if grad_dtype == "bf16" else 4) + 3 * 8 + (2 if publish else 0)
+
+
+def cpu_baseline_adamw(wl, budget_elems=1 << 24):
+    """fp64 AdamW oracle on whole tensors of the workload up to ~16 Mi elements."""
+    import oracle
+    from matrix_optimizer_muon_amd.workloads import make_adamw
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([p.get("num_threads", 1) for p in threadpool_info()
+                       if p.get("user_api") == "blas"] or [1])
+    except Exception:  # pragma: no cover
+        threads = os.cpu_count() or 1
+    total, n_el, n_t = 0.0, 0, 0
+    for t in wl.tensors:
+        if n_t and n_el + t.shape[0] > budget_elems:
+            break
+        ad = make_adamw(wl, t)
+        t1 = time.perf_counter()
+        oracle.adamw_step(ad.param, ad.grad, ad.exp_avg, ad.exp_avg_sq, lr=1e-3, beta1=0.9,
+                          beta2=0.999, eps=1e-8, wd=0.01, step=10)
+        total += time.perf_counter() - t1
+        n_el += t.shape[0]
+        n_t += 1
+    return {"value": n_el / total, "unit": "elements/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"{n_t} of {len(wl.tensors)} tensors ({n_el} elements), one step each in fp64 "
+                      f"numpy, {total:.3f} s", "seconds": total}
+
+
+def bench_adamw(args):
+    import numpy as np
+    import torch
+    import matrix_optimizer_muon_amd as mm
+    from matrix_optimizer_muon_amd.workloads import make_adamw, workload
+
+    name = args.workload if args.workload != DEFAULT_WORKLOAD else ADAMW_DEFAULT_WORKLOAD
+    wl = workload(name)
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    P, G, M, V, PUB = [], [], [], [], []
+    for t in wl.tensors:
+        ad = make_adamw(wl, t)
+        P.append(torch.from_numpy(ad.param).to(dev))
+        if ad.grad_bits is not None:
+            G.append(torch.from_numpy(ad.grad_bits.view(np.int16)).view(torch.bfloat16).to(dev))
+        else:
+            G.append(torch.from_numpy(ad.grad).to(dev))
+        M.append(torch.from_numpy(ad.exp_avg).to(dev))
+        V.append(torch.from_numpy(ad.exp_avg_sq).to(dev))
+        PUB.append(torch.empty(t.shape, dtype=torch.int16, device=dev))
+    pubs = PUB if args.publish else None
+    numel = sum(int(p.numel()) for p in P)
+    ws = torch.empty(1 << 20, dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream()
+    k = [10]
+    prepared = mm.AdamwStep(P, G, M, V, param_outs=pubs, workspace=ws)
+
+    def step():
+        prepared(k[0], stream)
+        k[0] += 1
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    if not args.no_phase_timing:
+        mm.phase_timing(True)
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    ev0.record(stream)
+    for _ in range(args.steps):
+        step()
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    mm.phase_timing(False)
+    phases = mm.phase_timing_read()
+    ms_step = ev0.elapsed_time(ev1) / args.steps
+    bpe = adamw_bytes_per_elem(wl.tensors[0].grad_dtype, args.publish)
+    roof = None
+    ms_tot, cnt = phases["adamw"]
+    if cnt:
+        avg_ms = ms_tot / cnt
+        ach = numel * bpe / (avg_ms * 1e-3) / 1e9
+        roof = {"kernel": "adamw", "bound": "hbm", "achieved": round(ach, 1), "peak": PEAK_HBM_GBS,
+                "unit": "GB/s", "frac": round(ach / PEAK_HBM_GBS, 4),
+                "traffic": measured_traffic("adamw", name), "avg_launch_ms": round(avg_ms, 4),
+                "bytes_per_launch": numel * bpe, "bytes_per_element": bpe, "launches": cnt}
+    cpu = None if args.no_cpu_baseline else cpu_baseline_adamw(wl)
+    line = {
+        "metric": ADAMW_METRIC, "value": round(numel / (ms_step * 1e-3), 1), "unit": "elements/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": name, "tensors": len(wl.tensors), "elements": numel,
+                   "grad_dtype": wl.tensors[0].grad_dtype, "publish": bool(args.publish)},
+        "roofline": roof, "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -162,6 +271,9 @@ def main():
     ap.add_argument("--precision", default="bf16", choices=["bf16", "f32"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-phase-timing", action="store_true")
+    ap.add_argument("--route", default="muon", choices=["muon", "adamw"])
+    ap.add_argument("--publish", action="store_true",
+                    help="also write the bf16 published copy of the updated parameters")
     ap.add_argument("--copy-probe", type=int, default=0,
                     help="only run a plain device copy of this many bytes (counter calibration)")
     args = ap.parse_args()
@@ -173,6 +285,9 @@ def main():
         print("bench.py measures one GPU only: the owner-rank step has no cross-GPU work on its "
               "hot path (each GPU steps its own LPT share); run with --gpus 1", file=sys.stderr)
         sys.exit(2)
+    if args.route == "adamw":
+        bench_adamw(args)
+        return
 
     import numpy as np
     import torch
@@ -183,7 +298,7 @@ def main():
     ts = matrices_of(wl, share)
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
-    grads, moms, masters = [], [], []
+    grads, moms, masters, pubs = [], [], [], []
     for t in ts:
         td = make_tensor(wl, t)
         if td.grad_bits is not None:
@@ -193,13 +308,18 @@ def main():
         grads.append(g)
         moms.append(torch.from_numpy(td.momentum).to(dev))
         masters.append(torch.from_numpy(td.master).to(dev))
+        if args.publish:
+            pubs.append(torch.empty(t.shape, dtype=torch.int16, device=dev))
         del td
     need = mm.muon_step_workspace_size(grads, moms, masters, precision=args.precision)
     ws = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
     stream = torch.cuda.current_stream()
 
+    prepared = mm.MuonStep(grads, moms, masters, precision=args.precision, workspace=ws,
+                           param_outs=pubs if args.publish else None)
+
     def step():
-        mm.muon_step(grads, moms, masters, precision=args.precision, workspace=ws, stream=stream)
+        prepared(stream)
 
     for _ in range(args.warmup):
         step()
@@ -257,7 +377,7 @@ def main():
         "pct_bf16_peak": round(100 * tflops / PEAK_BF16_TFLOPS, 2),
         "config": {"workload": args.workload, "matrices": slices, "shapes": shapes,
                    "ns_steps": HYPER["steps"], "grad_dtype": ts[0].grad_dtype,
-                   "effective_gflop_per_step": round(flops / 1e9, 1)},
+                   "effective_gflop_per_step": round(flops / 1e9, 1), "publish": bool(args.publish)},
         "roofline": roof,
         "cpu_baseline": cpu,
         "phases_ms_per_step": {k: round(v[0] / args.steps, 4) for k, v in phases.items() if v[1]},

@@ -34,8 +34,10 @@
  *   GPU entry point only ENQUEUES work on `stream` and returns; the caller keeps
  *   every buffer alive until that work completes.
  * - The caller owns and frees all memory, including the workspace.  The library
- *   allocates no device memory and keeps no state between calls, except the
- *   opt-in phase-timing events (dmuon_phase_timing).
+ *   allocates no device memory.  Between calls it keeps only the opt-in
+ *   phase-timing events (dmuon_phase_timing) and eight pinned host buffers
+ *   (with one event each) through which a call stages its tensor table to the
+ *   workspace, so that the host need not wait for the stream.
  * - Every argument is validated on the host, before anything is enqueued, so a
  *   rejected call leaves all buffers untouched.  Validation makes no HIP call.
  * - Return value: DMUON_OK or a negative DMUON_E_* code; dmuon_last_error()

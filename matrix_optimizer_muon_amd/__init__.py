@@ -16,7 +16,8 @@ import ctypes
 from . import _binding as _b
 from .workloads import HYPER  # noqa: F401
 
-__all__ = ["muon_step", "muon_step_workspace_size", "adamw_step", "ns_batched", "lpt_assign", "gemm_nt",
+__all__ = ["muon_step", "muon_step_workspace_size", "adamw_step", "MuonStep", "AdamwStep",
+           "ns_batched", "lpt_assign", "gemm_nt",
            "phase_timing", "phase_timing_read", "abi_version", "load_library", "HYPER"]
 
 QUINTIC = (HYPER["a"], HYPER["b"], HYPER["c"])
@@ -42,6 +43,45 @@ def muon_step_workspace_size(grads, momenta, masters, *, steps=5, precision="bf1
     return _b.muon_step_workspace_size(cfg, descs)
 
 
+class MuonStep:
+    """A prepared owner-rank Muon step over a fixed set of tensors.
+
+    The tensors are checked and marshalled once; every call enqueues one step
+    (``dmuon_muon_step``) on ``stream``.  The tensors must stay alive and keep
+    their storage; ``lr`` may be changed between calls.  Arguments as for
+    ``muon_step``.
+    """
+
+    def __init__(self, grads, momenta, masters, *, lr=HYPER["lr"], momentum=HYPER["mu"],
+                 weight_decay=HYPER["wd"], eps=HYPER["eps"], coeffs=QUINTIC, steps=HYPER["steps"],
+                 precision="bf16", grad_scale=1.0, ns_outs=None, param_outs=None, workspace=None):
+        self._tensors = (list(grads), list(momenta), list(masters), ns_outs, param_outs)
+        self.cfg = _b.make_cfg(lr, momentum, weight_decay, eps, coeffs, steps, precision, grad_scale)
+        self.arr, self.n = _b.make_descs(grads, momenta, masters, ns_outs, param_outs)
+        self.workspace = None
+        if self.n:
+            need = _b.muon_step_workspace_size(self.cfg, (self.arr, self.n))
+            if workspace is None:
+                workspace = _b.alloc_workspace(need, grads[0].device)
+            self.workspace = workspace
+
+    @property
+    def lr(self):
+        return self.cfg.lr
+
+    @lr.setter
+    def lr(self, value):
+        self.cfg.lr = value
+
+    def __call__(self, stream=None) -> None:
+        if self.n == 0:
+            return
+        ws = self.workspace
+        _b.check(_b.lib().dmuon_muon_step(self.arr, self.n, ctypes.byref(self.cfg),
+                                          ctypes.c_void_p(ws.data_ptr()),
+                                          ws.numel() * ws.element_size(), _b._stream_handle(stream)))
+
+
 def muon_step(grads, momenta, masters, *, lr=HYPER["lr"], momentum=HYPER["mu"],
               weight_decay=HYPER["wd"], eps=HYPER["eps"], coeffs=QUINTIC, steps=HYPER["steps"],
               precision="bf16", grad_scale=1.0, ns_outs=None, param_outs=None, workspace=None,
@@ -55,17 +95,47 @@ def muon_step(grads, momenta, masters, *, lr=HYPER["lr"], momentum=HYPER["mu"],
     workspace: optional uint8 GPU tensor of at least ``muon_step_workspace_size``
     bytes (allocated here when omitted).
     """
-    cfg = _b.make_cfg(lr, momentum, weight_decay, eps, coeffs, steps, precision, grad_scale)
-    arr, n = _b.make_descs(grads, momenta, masters, ns_outs, param_outs)
-    if n == 0:
-        return
-    need = _b.muon_step_workspace_size(cfg, (arr, n))
-    if workspace is None:
-        workspace = _b.alloc_workspace(need, grads[0].device)
-    L = _b.lib()
-    _b.check(L.dmuon_muon_step(arr, n, ctypes.byref(cfg), ctypes.c_void_p(workspace.data_ptr()),
-                               workspace.numel() * workspace.element_size(),
-                               _b._stream_handle(stream)))
+    MuonStep(grads, momenta, masters, lr=lr, momentum=momentum, weight_decay=weight_decay, eps=eps,
+             coeffs=coeffs, steps=steps, precision=precision, grad_scale=grad_scale,
+             ns_outs=ns_outs, param_outs=param_outs, workspace=workspace)(stream)
+
+
+class AdamwStep:
+    """A prepared ``adamw``-route step over a fixed set of tensors.
+
+    Marshals once; ``step_fn(step)`` enqueues one AdamW step with bias-correction
+    step number ``step`` (≥ 1).  Arguments as for ``adamw_step``.
+    """
+
+    def __init__(self, params, grads, exp_avgs, exp_avg_sqs, *, lr=1e-3, betas=(0.9, 0.999),
+                 eps=1e-8, weight_decay=0.01, grad_scale=1.0, param_outs=None, workspace=None):
+        self._tensors = (list(params), list(grads), list(exp_avgs), list(exp_avg_sqs), param_outs)
+        self.arr, self.n = _b.make_adamw_descs(params, grads, exp_avgs, exp_avg_sqs, param_outs)
+        self.cfg = _b.AdamwCfg(lr, betas[0], betas[1], eps, weight_decay, grad_scale, 1)
+        self.workspace = None
+        if self.n:
+            need = ctypes.c_size_t(0)
+            _b.check(_b.lib().dmuon_adamw_step_workspace_size(self.arr, self.n, ctypes.byref(need)))
+            if workspace is None:
+                workspace = _b.alloc_workspace(need.value, params[0].device)
+            self.workspace = workspace
+
+    @property
+    def lr(self):
+        return self.cfg.lr
+
+    @lr.setter
+    def lr(self, value):
+        self.cfg.lr = value
+
+    def __call__(self, step, stream=None) -> None:
+        if self.n == 0:
+            return
+        self.cfg.step = int(step)
+        ws = self.workspace
+        _b.check(_b.lib().dmuon_adamw_step(self.arr, self.n, ctypes.byref(self.cfg),
+                                           ctypes.c_void_p(ws.data_ptr()),
+                                           ws.numel() * ws.element_size(), _b._stream_handle(stream)))
 
 
 def adamw_step(params, grads, exp_avgs, exp_avg_sqs, *, step, lr=1e-3, betas=(0.9, 0.999),
@@ -77,18 +147,9 @@ def adamw_step(params, grads, exp_avgs, exp_avg_sqs, *, step, lr=1e-3, betas=(0.
     or fp32, read as grad_scale·grad; step ≥ 1 is the bias-correction step number;
     param_outs: optional bf16 tensors that receive the updated parameter.
     """
-    arr, n = _b.make_adamw_descs(params, grads, exp_avgs, exp_avg_sqs, param_outs)
-    if n == 0:
-        return
-    L = _b.lib()
-    need = ctypes.c_size_t(0)
-    _b.check(L.dmuon_adamw_step_workspace_size(arr, n, ctypes.byref(need)))
-    if workspace is None:
-        workspace = _b.alloc_workspace(need.value, params[0].device)
-    cfg = _b.AdamwCfg(lr, betas[0], betas[1], eps, weight_decay, grad_scale, int(step))
-    _b.check(L.dmuon_adamw_step(arr, n, ctypes.byref(cfg), ctypes.c_void_p(workspace.data_ptr()),
-                                workspace.numel() * workspace.element_size(),
-                                _b._stream_handle(stream)))
+    AdamwStep(params, grads, exp_avgs, exp_avg_sqs, lr=lr, betas=betas, eps=eps,
+              weight_decay=weight_decay, grad_scale=grad_scale, param_outs=param_outs,
+              workspace=workspace)(step, stream)
 
 
 def ns_batched(x, *, coeffs=QUINTIC, steps=HYPER["steps"], eps=HYPER["eps"], normalize=True,

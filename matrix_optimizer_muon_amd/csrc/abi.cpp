@@ -75,6 +75,46 @@ void timing_after(int phase, void* stream) {
 }
 
 // ---------------------------------------------------------------------------
+// table upload through pinned staging
+//
+// The per-call tensor table is copied host → device on the caller's stream.  A
+// copy from pageable memory may hold the host until the stream reaches it, so
+// the host could not enqueue ahead of the GPU.  The table is staged instead in
+// one of kStaging pinned buffers; an event recorded after each copy tells when
+// the buffer may be reused (by then it is long done: kStaging calls later).
+// ---------------------------------------------------------------------------
+constexpr int kStaging = 8;
+struct Staging {
+  void* host = nullptr;
+  size_t cap = 0;
+  hipEvent_t done = nullptr;
+};
+static std::mutex g_smu;
+static Staging g_stage[kStaging];
+static int g_stage_next = 0;
+
+static int stage_upload(void* dst, const void* src, size_t bytes, void* stream) {
+  std::lock_guard<std::mutex> lk(g_smu);
+  Staging& st = g_stage[g_stage_next];
+  g_stage_next = (g_stage_next + 1) % kStaging;
+  hipError_t e;
+  if (st.done && (e = hipEventSynchronize(st.done)) != hipSuccess) return (int)e;
+  if (st.cap < bytes) {
+    if (st.host && (e = hipHostFree(st.host)) != hipSuccess) return (int)e;
+    st.host = nullptr;
+    st.cap = 0;
+    const size_t cap = std::max<size_t>(bytes, 64 << 10);
+    if ((e = hipHostMalloc(&st.host, cap, hipHostMallocDefault)) != hipSuccess) return (int)e;
+    st.cap = cap;
+  }
+  std::memcpy(st.host, src, bytes);
+  if ((e = hipMemcpyAsync(dst, st.host, bytes, hipMemcpyHostToDevice, (hipStream_t)stream)) != hipSuccess)
+    return (int)e;
+  if (!st.done && (e = hipEventCreateWithFlags(&st.done, hipEventDisableTiming)) != hipSuccess) return (int)e;
+  return (int)hipEventRecord(st.done, (hipStream_t)stream);
+}
+
+// ---------------------------------------------------------------------------
 // planning
 // ---------------------------------------------------------------------------
 struct Item {
@@ -189,7 +229,7 @@ static int run_plan(Plan& pl, char* ws, int prec_f32, const LaunchScalars& base_
   std::vector<char> host(pl.table_bytes, 0);
   std::memcpy(host.data(), pl.probs.data(), pl.probs.size() * sizeof(DevProblem));
   std::memcpy(host.data() + pl.off_prefix, pl.prefix.data(), pl.prefix.size() * sizeof(int32_t));
-  int e = upload_async(ws, host.data(), host.size(), stream);
+  int e = stage_upload(ws, host.data(), host.size(), stream);
   if (e) return fail(DMUON_E_HIP, std::string("table upload: ") + hip_error_string(e));
   LaunchTable tab;
   tab.probs = (const DevProblem*)ws;
@@ -546,7 +586,7 @@ int dmuon_adamw_step(const dmuon_adamw_tensor* tensors, int32_t n, const dmuon_a
   std::memcpy(host.data(), pl.probs.data(), pl.probs.size() * sizeof(AdamwProblem));
   std::memcpy(host.data() + pl.off_prefix, pl.prefix.data(), pl.prefix.size() * sizeof(int32_t));
   char* ws = (char*)workspace;
-  e = upload_async(ws, host.data(), host.size(), stream);
+  e = stage_upload(ws, host.data(), host.size(), stream);
   if (e) return fail(DMUON_E_HIP, std::string("table upload: ") + hip_error_string(e));
   // bias corrections in double on the host (step is exact as an integer)
   const double b1 = cfg->beta1, b2 = cfg->beta2;

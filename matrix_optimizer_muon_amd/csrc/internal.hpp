@@ -123,7 +123,6 @@ int launch_gemm_nt(const void* A, const void* B, float* C, int64_t M, int64_t N,
                    int64_t lda, int64_t ldb, int64_t ldc, int f32, void* stream);
 int launch_adamw(const AdamwTable& tab, const AdamwScalars& s, void* stream);
 const char* hip_error_string(int err);
-int upload_async(void* dst, const void* src, size_t bytes, void* stream);
 
 // Phase timing (abi.cpp).
 void timing_before(int phase, void* stream);

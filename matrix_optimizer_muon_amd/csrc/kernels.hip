@@ -382,10 +382,12 @@ __global__ __launch_bounds__(kThreads) void k_adamw(AdamwTable tab, AdamwScalars
                        (!P.pub || ((uintptr_t)(P.pub + e0) & 15) == 0);
   int64_t done = e0;
   if (aligned) {
+    // 8 elements per vector; each pass handles kVec vectors per thread and
+    // issues all their loads before any store (the buffers may alias as far as
+    // the compiler knows, so it would not move loads above earlier stores)
+    constexpr int kVec = 2;
     const int64_t nvec = (e1 - e0) >> 3;
-    for (int64_t q = threadIdx.x; q < nvec; q += kThreads) {
-      const int64_t e = e0 + q * 8;
-      float g[8];
+    auto load_vec = [&](int64_t e, float (&g)[8], float (&pv)[8], float (&mv)[8], float (&vw)[8]) {
       if (P.grad_bf16) {
         const u32x4_t raw = *(const gptr<const u32x4_t>)(gb + e);
         const uint32_t w[4] = {raw.x, raw.y, raw.z, raw.w};
@@ -395,30 +397,51 @@ __global__ __launch_bounds__(kThreads) void k_adamw(AdamwTable tab, AdamwScalars
           g[2 * k + 1] = __uint_as_float(w[k] & 0xffff0000u);
         }
       } else {
-        const f32x4_t a = *(const gptr<const f32x4_t>)(gf + e), b = *(const gptr<const f32x4_t>)(gf + e + 4);
-        g[0] = a.x; g[1] = a.y; g[2] = a.z; g[3] = a.w; g[4] = b.x; g[5] = b.y; g[6] = b.z; g[7] = b.w;
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          const f32x4_t a = *(const gptr<const f32x4_t>)(gf + e + 4 * h);
+          g[4 * h] = a.x; g[4 * h + 1] = a.y; g[4 * h + 2] = a.z; g[4 * h + 3] = a.w;
+        }
       }
-      f32x4_t p4[2], m4[2], v4[2];
 #pragma unroll
       for (int h = 0; h < 2; ++h) {
-        p4[h] = *(const gptr<const f32x4_t>)(pp + e + 4 * h);
-        m4[h] = *(const gptr<const f32x4_t>)(mm + e + 4 * h);
-        v4[h] = *(const gptr<const f32x4_t>)(vv + e + 4 * h);
+        const f32x4_t a = *(const gptr<const f32x4_t>)(pp + e + 4 * h);
+        const f32x4_t b = *(const gptr<const f32x4_t>)(mm + e + 4 * h);
+        const f32x4_t c = *(const gptr<const f32x4_t>)(vv + e + 4 * h);
+        pv[4 * h] = a.x; pv[4 * h + 1] = a.y; pv[4 * h + 2] = a.z; pv[4 * h + 3] = a.w;
+        mv[4 * h] = b.x; mv[4 * h + 1] = b.y; mv[4 * h + 2] = b.z; mv[4 * h + 3] = b.w;
+        vw[4 * h] = c.x; vw[4 * h + 1] = c.y; vw[4 * h + 2] = c.z; vw[4 * h + 3] = c.w;
       }
-      float pv[8] = {p4[0].x, p4[0].y, p4[0].z, p4[0].w, p4[1].x, p4[1].y, p4[1].z, p4[1].w};
-      float mv[8] = {m4[0].x, m4[0].y, m4[0].z, m4[0].w, m4[1].x, m4[1].y, m4[1].z, m4[1].w};
-      float vv8[8] = {v4[0].x, v4[0].y, v4[0].z, v4[0].w, v4[1].x, v4[1].y, v4[1].z, v4[1].w};
-#pragma unroll
-      for (int k = 0; k < 8; ++k) adamw_elem(pv[k], mv[k], vv8[k], g[k], s);
+    };
+    auto store_vec = [&](int64_t e, const float (&pv)[8], const float (&mv)[8], const float (&vw)[8]) {
 #pragma unroll
       for (int h = 0; h < 2; ++h) {
         *(gptr<f32x4_t>)(pp + e + 4 * h) = f32x4_t{pv[4 * h], pv[4 * h + 1], pv[4 * h + 2], pv[4 * h + 3]};
         *(gptr<f32x4_t>)(mm + e + 4 * h) = f32x4_t{mv[4 * h], mv[4 * h + 1], mv[4 * h + 2], mv[4 * h + 3]};
-        *(gptr<f32x4_t>)(vv + e + 4 * h) = f32x4_t{vv8[4 * h], vv8[4 * h + 1], vv8[4 * h + 2], vv8[4 * h + 3]};
+        *(gptr<f32x4_t>)(vv + e + 4 * h) = f32x4_t{vw[4 * h], vw[4 * h + 1], vw[4 * h + 2], vw[4 * h + 3]};
       }
       if (pub)
         *(gptr<u32x4_t>)(pub + e) = u32x4_t{pack_bf16x2(pv[0], pv[1]), pack_bf16x2(pv[2], pv[3]),
                                             pack_bf16x2(pv[4], pv[5]), pack_bf16x2(pv[6], pv[7])};
+    };
+    int64_t q = threadIdx.x;
+    for (; q + (kVec - 1) * kThreads < nvec; q += kVec * kThreads) {
+      float g[kVec][8], pv[kVec][8], mv[kVec][8], vw[kVec][8];
+#pragma unroll
+      for (int u = 0; u < kVec; ++u) load_vec(e0 + (q + u * kThreads) * 8, g[u], pv[u], mv[u], vw[u]);
+#pragma unroll
+      for (int u = 0; u < kVec; ++u) {
+#pragma unroll
+        for (int k = 0; k < 8; ++k) adamw_elem(pv[u][k], mv[u][k], vw[u][k], g[u][k], s);
+        store_vec(e0 + (q + u * kThreads) * 8, pv[u], mv[u], vw[u]);
+      }
+    }
+    for (; q < nvec; q += kThreads) {
+      float g[8], pv[8], mv[8], vw[8];
+      load_vec(e0 + q * 8, g, pv, mv, vw);
+#pragma unroll
+      for (int k = 0; k < 8; ++k) adamw_elem(pv[k], mv[k], vw[k], g[k], s);
+      store_vec(e0 + q * 8, pv, mv, vw);
     }
     done = e0 + nvec * 8;
   }
@@ -1166,9 +1189,5 @@ int launch_gemm_nt(const void* A, const void* B, float* C, int64_t M, int64_t N,
 }
 
 const char* hip_error_string(int err) { return hipGetErrorString((hipError_t)err); }
-
-int upload_async(void* dst, const void* src, size_t bytes, void* stream) {
-  return (int)hipMemcpyAsync(dst, src, bytes, hipMemcpyHostToDevice, (hipStream_t)stream);
-}
 
 }  // namespace dmuon
