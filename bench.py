@@ -348,13 +348,16 @@ def main():
         dom = max(("gram", "square", "apply"), key=lambda p: phases[p][0])
         ms_tot, cnt = phases[dom]
         if cnt:
+            # the library may split the tensors into concurrent stream groups, each
+            # launch covering one group's slices: average over every launch
+            total_flops = pf[dom] * HYPER["steps"] * args.steps
             avg_ms = ms_tot / cnt
-            ach = pf[dom] / (avg_ms * 1e-3) / 1e12
+            ach = total_flops / (ms_tot * 1e-3) / 1e12
             roof = {"kernel": dom, "bound": "mfma", "achieved": round(ach, 2),
                     "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                     "frac": round(ach / PEAK_BF16_TFLOPS, 4),
                     "traffic": measured_traffic(dom, args.workload),
-                    "avg_launch_ms": round(avg_ms, 4), "flops_per_launch": pf[dom],
+                    "avg_launch_ms": round(avg_ms, 4), "flops_per_launch": round(total_flops / cnt),
                     "launches": cnt}
 
     cpu = None

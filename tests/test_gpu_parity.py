@@ -239,3 +239,19 @@ def test_step_merged_small_full():
     wl = workload("merged_small")
     tds = [make_tensor(wl, t) for t in wl.tensors]
     check_step(tds, "bf16", label="merged_small")
+
+
+def test_stream_groups_do_not_change_results(monkeypatch):
+    """Splitting the tensors over concurrent streams gives the same bits as one sequence."""
+    tds = [make_custom((600, 1000), "bf16", seed=(64, 0), scale=1e-3),
+           make_custom((1000, 600), "f32", seed=(64, 1)),
+           make_custom((3, 300, 520), "bf16", seed=(64, 2), scale=1e-3),
+           make_custom((257, 257), "f32", seed=(64, 3)),
+           make_custom((64, 64), "bf16", seed=(64, 4), scale=1e-3)]
+    runs = []
+    for groups in ("1", "3", "4"):
+        monkeypatch.setenv("DMUON_STREAM_GROUPS", groups)
+        runs.append(gpu_step(tds, "bf16"))
+    for other in runs[1:]:
+        for (b0, o0, w0), (b1, o1, w1) in zip(runs[0], other):
+            assert np.array_equal(b0, b1) and np.array_equal(o0, o1) and np.array_equal(w0, w1)
