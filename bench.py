@@ -35,14 +35,18 @@ DEFAULT_WORKLOAD = "layer_d2048"
 METRIC = "Muon NS step matrices/s + TFLOP/s and % bf16 MFMA peak, 1\u00d7MI355X"
 ADAMW_METRIC = "adamw route elements/s (owner 1-D parameters), 1\u00d7MI355X"
 ADAMW_DEFAULT_WORKLOAD = "adamw_stream"
-KERNELS_SRC = os.path.join(ROOT, "matrix_optimizer_muon_amd", "csrc", "kernels.hip")
+# sources that decide what a launch does: the kernels and the planner (grouping, tiling)
+KERNELS_SRC = [os.path.join(ROOT, "matrix_optimizer_muon_amd", "csrc", f) for f in ("kernels.hip", "abi.cpp")]
 PROFILES = os.path.join(ROOT, "profiles")
 
 
 def kernels_sha256():
     import hashlib
-    with open(KERNELS_SRC, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()
+    h = hashlib.sha256()
+    for path in KERNELS_SRC:
+        with open(path, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
 
 
 def measured_traffic(kernel, workload_name):
@@ -50,7 +54,7 @@ def measured_traffic(kernel, workload_name):
 
     The summary records FETCH_SIZE and WRITE_SIZE per dispatch, calibrated by the
     same counters on a plain device copy of known size, and the sha256 of the
-    kernel source they were taken on; a different source gives None.
+    kernel and planner sources they were taken on; a different source gives None.
     """
     path = os.path.join(PROFILES, f"traffic_{kernel}_{workload_name}.md")
     if not os.path.exists(path):
