@@ -239,16 +239,17 @@ int dmuon_gemm_nt(const void* A, const void* B, float* C, int64_t M, int64_t N, 
  * launch of the library is bracketed by two hipEvents on its stream; enable = 0
  * stops it.  dmuon_phase_timing_read waits for the recorded events, writes for
  * each phase p < n the summed milliseconds ms[p] and the launch count count[p],
- * then clears the record.  Phases: 0 momentum + partial norms, 1 start (scale +
- * operand copies), 2 Gram, 3 square+poly, 4 apply, 5 update (k = 0 only),
- * 6 gemm_nt, 7 norm finalize, 8 adamw. */
+ * then clears the record.  Phases: 0 ingest (momentum, partial norms, operand
+ * copies), 1 norm finalize, 2 Gram, 3 square+poly, 4 apply, 5 update (k = 0
+ * only), 6 gemm_nt, 7 adamw. */
 int dmuon_phase_timing(int32_t enable);
 int dmuon_phase_timing_read(double* ms, int64_t* count, int32_t n);
 
 /* Message for the last non-OK return on this thread ("" if none). */
 const char* dmuon_last_error(void);
 
-/* ABI version (bumped on any signature change). */
+/* ABI version (bumped on any change of a signature, a struct or a documented
+ * numbering such as the phases above). */
 int32_t dmuon_abi_version(void);
 
 #ifdef __cplusplus

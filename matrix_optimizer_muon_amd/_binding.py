@@ -27,12 +27,12 @@ ERRORS = {
 }
 F32, BF16 = 0, 1
 PREC = {"bf16": 0, "f32": 1}
-PHASES = ["momentum", "start", "gram", "square", "apply", "update", "gemm_nt", "norm", "adamw"]
+PHASES = ["ingest", "norm", "gram", "square", "apply", "update", "gemm_nt", "adamw"]
 EXPORTED = ["dmuon_muon_step_workspace_size", "dmuon_muon_step", "dmuon_ns_batched_workspace_size",
             "dmuon_ns_batched", "dmuon_lpt_assign", "dmuon_adamw_step_workspace_size",
             "dmuon_adamw_step", "dmuon_gemm_nt", "dmuon_phase_timing", "dmuon_phase_timing_read",
             "dmuon_last_error", "dmuon_abi_version"]
-ABI_VERSION = 2
+ABI_VERSION = 3
 
 
 class DmuonError(Exception):

@@ -198,17 +198,19 @@ static int build_plan(const std::vector<Item>& items, int prec_f32, Plan& pl, ch
     P.out = it.out;
     P.pub = it.pub;
     const int64_t b = it.batch;
+    const int64_t prep = (int64_t)P.prep_tiles_r * P.prep_tiles_c;
     P.xf = (float*)carve((size_t)(b * it.rows * P.ld_x) * 4);
     P.xg = carve((size_t)(b * P.m * P.ld_n) * esz);
     P.xa0 = carve((size_t)(b * P.n * P.ld_m) * esz);
     P.xa1 = carve((size_t)(b * P.n * P.ld_m) * esz);
     P.ap = carve((size_t)(b * P.m * P.ld_m) * esz);
     P.bp = carve((size_t)(b * P.m * P.ld_m) * esz);
-    P.part_norm = (float*)carve((size_t)(b * P.chunks) * 4);
+    P.part_norm = (float*)carve((size_t)(b * prep) * 4);
+    P.x0 = it.mom ? it.mom : P.xf;
+    P.ld_x0 = it.mom ? (int32_t)it.cols : P.ld_x;
     P.part_apply = (float*)carve((size_t)(b * P.apply_tr * P.apply_tc) * 4);
     const int64_t tri = (int64_t)P.tiles_m * (P.tiles_m + 1) / 2;
-    const int64_t cnt[PH_COUNT] = {b * P.chunks, b * P.prep_tiles_r * P.prep_tiles_c, b * tri, b * tri,
-                                   b * P.apply_tr * P.apply_tc, b * P.chunks, 0, b, 0};
+    const int64_t cnt[PH_COUNT] = {b * prep, b, b * tri, b * tri, b * P.apply_tr * P.apply_tc, b * P.chunks, 0, 0};
     for (int ph = 0; ph < PH_COUNT; ++ph) {
       P.wg0[ph] = (int32_t)wg[ph];
       pl.prefix[(size_t)ph * (n + 1) + i] = (int32_t)wg[ph];
@@ -245,9 +247,8 @@ static int run_plan(Plan& pl, char* ws, int prec_f32, const LaunchScalars& base_
   LaunchScalars s = base_s;
   s.t = 0;
   s.last = 0;
-  if ((e = go(PH_MOMENTUM, s))) return e;
+  if ((e = go(PH_INGEST, s))) return e;
   if ((e = go(PH_NORM, s))) return e;
-  if ((e = go(PH_START, s))) return e;
   if (steps == 0) return go(PH_UPDATE, s);
   for (int t = 0; t < steps; ++t) {
     s.t = t;
@@ -572,7 +573,7 @@ using namespace dmuon;
 
 extern "C" {
 
-int32_t dmuon_abi_version(void) { return 2; }
+int32_t dmuon_abi_version(void) { return 3; }
 
 const char* dmuon_last_error(void) { return g_err.c_str(); }
 

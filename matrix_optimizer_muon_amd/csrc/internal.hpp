@@ -12,22 +12,21 @@ namespace dmuon {
 constexpr int kThreads = 256;          // threads per workgroup (4 wave64)
 constexpr int kTile = 256;             // output tile edge of the contraction kernels
 constexpr int kElemChunk = 16384;      // elements per workgroup of the momentum kernel
-constexpr int kPrepTile = 64;          // tile edge of the start (scale + copies) kernel
+constexpr int kPrepTile = 64;          // tile edge of the ingest kernel
 constexpr int kLdAlign = 64;           // operand leading dims are multiples of this
 constexpr int kMaxSteps = 64;          // ns_steps upper bound
 constexpr int kScalStride = 80;        // floats of per-slice scalars (inv, d[0..k])
 
 enum Phase : int {
-  PH_MOMENTUM = 0,   // momentum + sum of squares
-  PH_START = 1,      // X0 = inv * B, operand copies
+  PH_INGEST = 0,     // momentum, partial sums of squares, unscaled operand copies
+  PH_NORM = 1,       // per-slice norm finalize: inv = 1/(‖B‖_F + eps), d₀
   PH_GRAM = 2,       // A' = X Xᵀ − d I (upper tiles, mirrored)
   PH_SQUARE = 3,     // B' = (b + 2cd) A' + c A'²
   PH_APPLY = 4,      // X ← (a + bd + cd²) X + B' X (last: decay + update)
   PH_UPDATE = 5,     // W ← (1 − lr wd) W − lr X0 (only when k = 0)
   PH_GEMM = 6,       // test hook: plain NT product
-  PH_NORM = 7,       // per-slice norm finalize: inv = 1/(‖B‖_F + eps), d₀
-  PH_ADAMW = 8,      // the adamw route (its own launch table)
-  PH_COUNT = 9
+  PH_ADAMW = 7,      // the adamw route (its own launch table)
+  PH_COUNT = 8
 };
 
 // One tensor (2-D = batch 1, or 3-D batch of slices) as the kernels see it.
@@ -40,21 +39,23 @@ struct DevProblem {
   int32_t ld_m;                // round_up(m, 64): ld of XA, A', B' (n×ld_m, m×ld_m)
   int32_t ld_n;                // round_up(n, 64): ld of XG (m×ld_n)
   int32_t grad_bf16;           // 1: grad is bf16, 0: fp32
-  int32_t chunks;              // momentum-kernel workgroups per slice
-  int32_t prep_tiles_r, prep_tiles_c;   // start-kernel 64×64 tiles per slice
+  int32_t chunks;              // update-kernel workgroups per slice (k = 0)
+  int32_t prep_tiles_r, prep_tiles_c;   // ingest-kernel 64×64 tiles per slice
   int32_t tiles_m;             // ceil(m / 256)
   int32_t apply_tr, apply_tc;  // apply tiles per slice over rows / cols of storage
   int32_t slice_base;          // global index of this problem's first slice
   int32_t ld_x;                // round_up(cols, 32): ld of the fp32 iterate
   // per-phase workgroup prefix (first global workgroup of this problem)
   int32_t wg0[PH_COUNT];
-  int32_t pad1;
+  int32_t ld_x0;               // ld of x0
   // caller buffers (slice stride = rows*cols)
-  const void* grad;            // momentum-kernel input (grad, or x for ns_batched)
+  const void* grad;            // ingest input (grad, or x for ns_batched)
   float* mom;                  // momentum (NULL for ns_batched)
   float* master;               // master weight (NULL for ns_batched)
   float* out;                  // NS output (NULL if not wanted)
   uint16_t* pub;               // bf16 published parameter (NULL if not wanted)
+  const float* x0;             // X₀ before its 1/(‖B‖_F + eps) scale: the momentum
+                               // (ld cols), or for ns_batched x in the iterate buffer
   // workspace (operand element type = bf16 or fp32 per precision)
   float* xf;                   // fp32 iterate, storage layout rows×ld_x, stride rows*ld_x
   void* xg;                    // oriented X, m×ld_n, stride m*ld_n
@@ -62,7 +63,7 @@ struct DevProblem {
   void* xa1;                   // (pong)
   void* ap;                    // A', m×ld_m, stride m*ld_m
   void* bp;                    // B', m×ld_m
-  float* part_norm;            // [batch][chunks]
+  float* part_norm;            // [batch][prep_tiles_r*prep_tiles_c]
   float* part_apply;           // [batch][apply_tr*apply_tc]
 };
 

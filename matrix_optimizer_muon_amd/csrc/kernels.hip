@@ -4,9 +4,10 @@
 // owner-local step) is run as one grouped launch per phase over every 2-D slice
 // of every tensor:
 //
-//   momentum   B ← μB + G, per-workgroup partial Σ B² (HBM stream)
-//   start      X₀ = B / (‖B‖_F + eps) → fp32 iterate + two operand copies
-//              (oriented X row-major and its transpose), zero padding
+//   ingest     B ← μB + s·G, per-tile partial Σ B², and the operand copies of
+//              B (oriented row-major and its transpose, zero padded)
+//   norm       inv = 1/(‖B‖_F + eps), X₀ = inv·B (the scale is folded into the
+//              first Gram and the first apply)
 //   k × { gram    A' = X Xᵀ − d·I          (upper 256×256 tiles, mirrored)
 //         square  B' = (b + 2cd)·A' + c·A'²  (upper tiles, mirrored)
 //         apply   X ← (a + bd + cd²)·X + B'·X; the last one fuses
@@ -96,82 +97,8 @@ __device__ __forceinline__ float sum_partials(const float* part, int count, floa
   return block_sum<W>(v, red);
 }
 
-// ---------------------------------------------------------------------------
-// momentum: B ← μB + G (or, for NS alone, just read x) and partial Σ B²
-// ---------------------------------------------------------------------------
-__global__ __launch_bounds__(kThreads) void k_momentum(LaunchTable tab, LaunchScalars s) {
-  __shared__ float red[4];
-  const int bid = blockIdx.x;
-  const int p = find_prob(tab.wg_prefix + PH_MOMENTUM * (tab.n_probs + 1), tab.n_probs, bid);
-  const DevProblem& P = tab.probs[p];
-  const int local = bid - P.wg0[PH_MOMENTUM];
-  const int slice = local / P.chunks, chunk = local % P.chunks;
-  const int64_t per = (int64_t)P.rows * P.cols;
-  const int64_t base = (int64_t)slice * per;
-  const int64_t e0 = (int64_t)chunk * kElemChunk;
-  const int64_t e1 = (e0 + kElemChunk < per) ? e0 + kElemChunk : per;
-  const float mu = s.mu;
-  float* mom = s.has_momentum ? P.mom + base : nullptr;
-  const uint16_t* gb = (const uint16_t*)P.grad + base;
-  const float* gf = (const float*)P.grad + base;
-  float acc = 0.f;
-
-  const bool aligned =
-      ((P.grad_bf16 ? ((uintptr_t)(gb + e0) & 15) : ((uintptr_t)(gf + e0) & 15)) == 0) &&
-      (!mom || (((uintptr_t)(mom + e0) & 15) == 0));
-  int64_t done = e0;
-  if (aligned) {
-    const int64_t nvec = (e1 - e0) >> 3;
-    for (int64_t g = threadIdx.x; g < nvec; g += kThreads) {
-      const int64_t e = e0 + g * 8;
-      float x[8];
-      if (P.grad_bf16) {
-        const uint4 raw = *(const uint4*)(gb + e);
-        const uint32_t w[4] = {raw.x, raw.y, raw.z, raw.w};
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          x[2 * q] = __uint_as_float(w[q] << 16);
-          x[2 * q + 1] = __uint_as_float(w[q] & 0xffff0000u);
-        }
-      } else {
-        const float4 u = *(const float4*)(gf + e), v = *(const float4*)(gf + e + 4);
-        x[0] = u.x; x[1] = u.y; x[2] = u.z; x[3] = u.w;
-        x[4] = v.x; x[5] = v.y; x[6] = v.z; x[7] = v.w;
-      }
-      if (mom) {
-#pragma unroll
-        for (int i = 0; i < 8; ++i) x[i] *= s.gscale;
-        float4 u = *(const float4*)(mom + e), v = *(const float4*)(mom + e + 4);
-        u.x = fmaf(mu, u.x, x[0]); u.y = fmaf(mu, u.y, x[1]);
-        u.z = fmaf(mu, u.z, x[2]); u.w = fmaf(mu, u.w, x[3]);
-        v.x = fmaf(mu, v.x, x[4]); v.y = fmaf(mu, v.y, x[5]);
-        v.z = fmaf(mu, v.z, x[6]); v.w = fmaf(mu, v.w, x[7]);
-        *(float4*)(mom + e) = u;
-        *(float4*)(mom + e + 4) = v;
-        x[0] = u.x; x[1] = u.y; x[2] = u.z; x[3] = u.w;
-        x[4] = v.x; x[5] = v.y; x[6] = v.z; x[7] = v.w;
-      }
-      float q = 0.f;
-#pragma unroll
-      for (int i = 0; i < 8; ++i) q = fmaf(x[i], x[i], q);
-      acc += q;
-    }
-    done = e0 + nvec * 8;
-  }
-  for (int64_t e = done + threadIdx.x; e < e1; e += kThreads) {
-    float x = P.grad_bf16 ? bf16_to_f32(gb[e]) : gf[e];
-    if (mom) {
-      x = fmaf(mu, mom[e], s.gscale * x);
-      mom[e] = x;
-    }
-    acc = fmaf(x, x, acc);
-  }
-  const float tot = block_sum<4>(acc, red);
-  if (threadIdx.x == 0) P.part_norm[(int64_t)slice * P.chunks + chunk] = tot;
-}
-
-// Store 4 consecutive elements (rows gr0..gr0+3 of the tile, one column) as one
-// vector into a transposed row: dst[col][gr0 .. gr0+3].
+// Store 4 consecutive elements of one destination row as one vector (8 bytes of
+// bf16 or 16 bytes of fp32).
 __device__ __forceinline__ void store4(uint16_t* p, float a, float b, float c, float d) {
   const uint32_t lo = (uint32_t)f32_to_bf16(a) | ((uint32_t)f32_to_bf16(b) << 16);
   const uint32_t hi = (uint32_t)f32_to_bf16(c) | ((uint32_t)f32_to_bf16(d) << 16);
@@ -210,10 +137,10 @@ __device__ __forceinline__ void store_row16(uint16_t* p, const float (&v)[8]) {
 __device__ __forceinline__ void store_row16(float* p, const float (&v)[4]) {
   *(float4*)p = make_float4(v[0], v[1], v[2], v[3]);
 }
-
 // ---------------------------------------------------------------------------
-// norm finalize: one workgroup per slice sums the momentum kernel's partials in
-// a fixed order: inv = 1/(‖B‖_F + eps) (1 without normalisation), d₀ = ‖X₀‖²_F/m
+// norm finalize: one workgroup per slice sums the ingest kernel's per-tile
+// partials in a fixed order: inv = 1/(‖B‖_F + eps) (1 without normalisation),
+// d₀ = ‖X₀‖²_F/m = inv²·‖B‖²_F/m
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(kThreads) void k_norm(LaunchTable tab, LaunchScalars s) {
   __shared__ float red[4];
@@ -221,102 +148,133 @@ __global__ __launch_bounds__(kThreads) void k_norm(LaunchTable tab, LaunchScalar
   const int p = find_prob(tab.wg_prefix + PH_NORM * (tab.n_probs + 1), tab.n_probs, bid);
   const DevProblem& P = tab.probs[p];
   const int slice = bid - P.wg0[PH_NORM];
-  const float total = sum_partials<4>(P.part_norm + (int64_t)slice * P.chunks, P.chunks, red);
+  const int cnt = P.prep_tiles_r * P.prep_tiles_c;
+  const float total = sum_partials<4>(P.part_norm + (int64_t)slice * cnt, cnt, red);
   if (threadIdx.x == 0) {
     const float inv = s.normalize ? 1.0f / (sqrtf(total) + s.eps) : 1.0f;
     float* scal = tab.scal + (int64_t)(P.slice_base + slice) * kScalStride;
     scal[0] = inv;
-    scal[1] = total * inv * inv / (float)P.m;   // d₀ = ‖X₀‖²_F / m
+    scal[1] = total * inv * inv / (float)P.m;
   }
 }
 
 // ---------------------------------------------------------------------------
-// start: X₀ = inv·B into the fp32 iterate (storage layout), the operand copy in
-// storage layout, and the transposed operand copy through a 64×64 LDS tile; zero
-// padding up to the 64-element leading dims.  All global accesses are 16-byte
-// (or 8-byte for a bf16 copy) row vectors when the row length allows.
+// ingest: one 64×64 storage tile of one slice per workgroup
+//   B ← μB + s·G into the momentum (for NS alone X = x, kept in fp32 in the
+//   iterate buffer), the tile's partial Σ B², and the operand copies of B in
+//   storage layout and transposed (through an LDS tile), unscaled, with zero
+//   padding up to the 64-element leading dims.
+// The scale of X₀ = inv·B, inv = 1/(‖B‖_F + eps), is applied by the first Gram
+// (A'₀ = inv²·B Bᵀ − d₀·I) and the first apply (X₁ = inv·(α·B + B'₀·B)), which
+// is the same algebra, so B is read once and no scaled copy of it is written.
+// Global accesses are 16-byte row vectors (8-byte for bf16 data) when the row
+// length allows; every load of the tile is issued before the first store.
 // ---------------------------------------------------------------------------
 template <typename T>
-__global__ __launch_bounds__(kThreads) void k_start(LaunchTable tab, LaunchScalars s) {
+__global__ __launch_bounds__(kThreads) void k_ingest(LaunchTable tab, LaunchScalars s) {
   __shared__ float tile[kPrepTile][kPrepTile + 1];
+  __shared__ float red[4];
   const int bid = blockIdx.x;
-  const int p = find_prob(tab.wg_prefix + PH_START * (tab.n_probs + 1), tab.n_probs, bid);
+  const int p = find_prob(tab.wg_prefix + PH_INGEST * (tab.n_probs + 1), tab.n_probs, bid);
   const DevProblem& P = tab.probs[p];
-  const int local = bid - P.wg0[PH_START];
+  const int local = bid - P.wg0[PH_INGEST];
   const int per_slice = P.prep_tiles_r * P.prep_tiles_c;
   const int slice = local / per_slice, tt = local % per_slice;
   const int r0 = (tt / P.prep_tiles_c) * kPrepTile, c0 = (tt % P.prep_tiles_c) * kPrepTile;
   const int rows = P.rows, cols = P.cols;
-  const float inv = tab.scal[(int64_t)(P.slice_base + slice) * kScalStride];
-
   const int64_t per = (int64_t)rows * cols;
-  const float* srcf = s.has_momentum ? P.mom + (int64_t)slice * per
-                                     : (P.grad_bf16 ? nullptr : (const float*)P.grad + (int64_t)slice * per);
-  const uint16_t* srcb = (!s.has_momentum && P.grad_bf16) ? (const uint16_t*)P.grad + (int64_t)slice * per
-                                                          : nullptr;
-  float* xf = P.xf + (int64_t)slice * rows * P.ld_x;
+  const uint16_t* gb = (const uint16_t*)P.grad + (int64_t)slice * per;
+  const float* gf = (const float*)P.grad + (int64_t)slice * per;
+  float* mom = s.has_momentum ? P.mom + (int64_t)slice * per : nullptr;
+  float* xf = s.has_momentum ? nullptr : P.xf + (int64_t)slice * rows * P.ld_x;
   const int ld_s = P.wide ? P.ld_n : P.ld_m;    // straight copy: cols padded
   const int ld_t = P.wide ? P.ld_m : P.ld_n;    // transposed copy: rows padded
   T* cs = (T*)(P.wide ? P.xg : P.xa0) + (int64_t)slice * rows * ld_s;
   T* ct = (T*)(P.wide ? P.xa0 : P.xg) + (int64_t)slice * cols * ld_t;
-  // rows of 4-element vectors are aligned when cols is a multiple of 4 (and the
-  // source pointer is 16-byte aligned; bf16 sources need 8 bytes)
+  // rows of 4-element vectors are aligned when cols is a multiple of 4 and the
+  // slice bases are (16 bytes for fp32 data, 8 for bf16)
   const bool vec = (cols & 3) == 0 &&
-                   (srcb ? (((uintptr_t)srcb & 7) == 0) : (((uintptr_t)srcf & 15) == 0));
+                   ((P.grad_bf16 ? ((uintptr_t)gb & 7) : ((uintptr_t)gf & 15)) == 0) &&
+                   (!mom || ((uintptr_t)mom & 15) == 0);
 
   const int tr = threadIdx.x >> 4;          // 0..15
   const int tc = (threadIdx.x & 15) * 4;    // 0..60
+  const int c = c0 + tc;
+  // (1) loads: rows r0 + 16q + tr, columns c .. c+3; zero outside the slice
+  float g[4][4], b[4][4];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const int r = r0 + q * 16 + tr;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) g[q][e] = b[q][e] = 0.f;
+    if (r >= rows) continue;
+    const int64_t o = (int64_t)r * cols + c;
+    if (vec) {
+      if (c < cols) {
+        if (P.grad_bf16) load4(gb + o, g[q]); else load4(gf + o, g[q]);
+        if (mom) load4(mom + o, b[q]);
+      }
+    } else {
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        if (c + e < cols) {
+          g[q][e] = P.grad_bf16 ? bf16_to_f32(gb[o + e]) : gf[o + e];
+          if (mom) b[q][e] = mom[o + e];
+        }
+    }
+  }
+  // (2) the new B, stored to the momentum (or the fp32 x) and the straight copy
+  float sq = 0.f;
 #pragma unroll
   for (int q = 0; q < 4; ++q) {
     const int lr = q * 16 + tr;
     const int r = r0 + lr;
-    const int c = c0 + tc;
-    float v[4] = {0.f, 0.f, 0.f, 0.f};
+    float v[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      v[e] = mom ? fmaf(s.mu, b[q][e], s.gscale * g[q][e]) : g[q][e];
+      sq = fmaf(v[e], v[e], sq);
+    }
     if (r < rows) {
       const int64_t o = (int64_t)r * cols + c;
-      if (vec && c + 3 < cols) {
-        if (srcb) {
-          const uint2 u = *(const uint2*)(srcb + o);
-          v[0] = __uint_as_float(u.x << 16); v[1] = __uint_as_float(u.x & 0xffff0000u);
-          v[2] = __uint_as_float(u.y << 16); v[3] = __uint_as_float(u.y & 0xffff0000u);
+      if (mom) {
+        if (vec) {
+          if (c < cols) *(float4*)(mom + o) = make_float4(v[0], v[1], v[2], v[3]);
         } else {
-          const float4 u = *(const float4*)(srcf + o);
-          v[0] = u.x; v[1] = u.y; v[2] = u.z; v[3] = u.w;
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            if (c + e < cols) mom[o + e] = v[e];
         }
-      } else {
-#pragma unroll
-        for (int e = 0; e < 4; ++e)
-          if (c + e < cols) v[e] = srcb ? bf16_to_f32(srcb[o + e]) : srcf[o + e];
       }
-#pragma unroll
-      for (int e = 0; e < 4; ++e) v[e] *= inv;
-      if (c < cols) *(float4*)(xf + (int64_t)r * P.ld_x + c) = make_float4(v[0], v[1], v[2], v[3]);
+      if (xf && c < cols) *(float4*)(xf + (int64_t)r * P.ld_x + c) = make_float4(v[0], v[1], v[2], v[3]);
       if (c < ld_s) store4(cs + (int64_t)r * ld_s + c, v[0], v[1], v[2], v[3]);
     }
 #pragma unroll
     for (int e = 0; e < 4; ++e) tile[lr][tc + e] = v[e];
   }
-  __syncthreads();
-  // transposed copy: 64 storage columns × 64 storage rows = 8 chunks of 8 rows
-  // (bf16) or 16 chunks of 4 rows (fp32) per column
+  // (3) the tile's Σ B² (its barriers also publish the LDS tile)
+  const float tot = block_sum<4>(sq, red);
+  if (threadIdx.x == 0) P.part_norm[(int64_t)slice * per_slice + tt] = tot;
+  // (4) transposed copy: 64 storage columns × 64 storage rows = 8 chunks of 8
+  // rows (bf16) or 16 chunks of 4 rows (fp32) per column
   constexpr int RPC = 16 / (int)sizeof(T);
   constexpr int CPC = kPrepTile / RPC;
 #pragma unroll
   for (int k = 0; k < (kPrepTile * CPC) / kThreads; ++k) {
     const int id = threadIdx.x + kThreads * k;
     const int lc = id / CPC, rg = id % CPC;
-    const int c = c0 + lc;                  // storage column = transposed row
+    const int cc = c0 + lc;                 // storage column = transposed row
     const int r = r0 + rg * RPC;            // first storage row = transposed column
-    if (c >= cols || r >= ld_t) continue;
+    if (cc >= cols || r >= ld_t) continue;
     float v[RPC];
 #pragma unroll
     for (int e = 0; e < RPC; ++e) v[e] = tile[rg * RPC + e][lc];
-    store_row16(ct + (int64_t)c * ld_t + r, v);
+    store_row16(ct + (int64_t)cc * ld_t + r, v);
   }
 }
 
 // ---------------------------------------------------------------------------
-// update when k = 0: W ← (1 − lr·wd)·W − lr·X₀, out = X₀
+// update when k = 0: W ← (1 − lr·wd)·W − lr·X₀, out = X₀ = inv·B
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(kThreads) void k_update(LaunchTable tab, LaunchScalars s) {
   const int bid = blockIdx.x;
@@ -326,12 +284,13 @@ __global__ __launch_bounds__(kThreads) void k_update(LaunchTable tab, LaunchScal
   const int slice = local / P.chunks, chunk = local % P.chunks;
   const int64_t per = (int64_t)P.rows * P.cols;
   const int64_t base = (int64_t)slice * per;
-  const float* xf = P.xf + (int64_t)slice * P.rows * P.ld_x;
+  const float inv = tab.scal[(int64_t)(P.slice_base + slice) * kScalStride];
+  const float* x0 = P.x0 + (int64_t)slice * P.rows * P.ld_x0;
   const int64_t e0 = (int64_t)chunk * kElemChunk;
   const int64_t e1 = (e0 + kElemChunk < per) ? e0 + kElemChunk : per;
   for (int64_t e = e0 + threadIdx.x; e < e1; e += kThreads) {
     const int64_t r = e / P.cols, c = e - r * P.cols;
-    const float x = xf[r * P.ld_x + c];
+    const float x = inv * x0[r * P.ld_x0 + c];
     if (P.out) P.out[base + e] = x;
     if (s.write_master) {
       const float w = fmaf(-s.lr, x, s.decay * P.master[base + e]);
@@ -675,12 +634,12 @@ __device__ __forceinline__ int xcd_logical_block() {
 // ---- Gram / square epilogue.  Each 128-row half of the tile is staged in LDS
 // (fp32); a row pass writes the row-major block with 8- or 16-byte vectors and a
 // column pass writes the mirrored block of an off-diagonal tile.
-//   Gram:   A' = acc − d·I
+//   Gram:   A' = xs²·acc − d·I   (xs = inv at t = 0, whose operands are B; else 1)
 //   square: B' = (b + 2cd)·A' + c·acc   (acc = A'·A'ᵀ = A'² since A' is symmetric)
 template <typename T, int PH>
 __device__ __forceinline__ void sym_epilogue(const DevProblem& P, const LaunchScalars& s,
                                              f32x16_t (&acc)[4][2], char* smem, int slice, int ti,
-                                             int tj, int row0, int col0, float d) {
+                                             int tj, int row0, int col0, float d, float xs) {
   const int tid = threadIdx.x;
   const int m = P.m, ldm = P.ld_m;
   T* dst = (T*)(PH == PH_GRAM ? P.ap : P.bp) + (int64_t)slice * m * ldm;
@@ -735,9 +694,12 @@ __device__ __forceinline__ void sym_epilogue(const DevProblem& P, const LaunchSc
         const int gr = row0 + hf * 128 + rr, gc = col0 + 4 * cq;
         const bool rok = gr < m;
         if (PH == PH_GRAM) {
+          const float gsc = xs * xs;
 #pragma unroll
-          for (int e = 0; e < 4; ++e)
+          for (int e = 0; e < 4; ++e) {
+            v[e] *= gsc;
             if (gr == gc + e && rok) v[e] -= d;
+          }
         } else {
           float ap[4];
           if (sizeof(T) == 2) {
@@ -809,8 +771,10 @@ typedef unsigned u32x2_t __attribute__((ext_vector_type(2)));
 // Lane (h, r32) of wave (wr, wc) holds, for block (i, j) and register r = 4·rq + e,
 // the element at tile row 128·wr + 32·i + 8·rq + 4·h + e and tile column
 // 64·wc + 32·j + r32.  Per block:
-//   X' = α·X + acc (fp32 iterate, read and written with 4-byte accesses: each
-//        wave instruction covers two 128-byte row segments), α = a + b·d + c·d²
+//   X' = xs·(α·X + acc) (fp32 iterate, read and written with 4-byte accesses:
+//        each wave instruction covers two 128-byte row segments), α = a + b·d + c·d²;
+//        at t = 0 X is read from the unscaled source x0 (B) and xs = inv, else
+//        xs = 1
 //   t < k−1: the row-major operand copy, two columns per dword (even lanes take
 //        rows e = 0, 2 from their odd neighbour, odd lanes rows 1, 3), and the
 //        transposed copy, four consecutive rows per store; Σ X'² partial
@@ -824,7 +788,7 @@ typedef unsigned u32x2_t __attribute__((ext_vector_type(2)));
 template <typename T, bool LAST>
 __device__ __forceinline__ void apply_epilogue(const DevProblem& P, const LaunchScalars& s,
                                                f32x16_t (&acc)[4][2], int slice, int u, int row0,
-                                               int col0, float d, float* red) {
+                                               int col0, float d, float xs, float* red) {
   constexpr int kAhead = LAST ? 2 : 3;
   constexpr unsigned E = sizeof(T);
   const int lane = threadIdx.x & 63;
@@ -845,6 +809,15 @@ __device__ __forceinline__ void apply_epilogue(const DevProblem& P, const Launch
 #pragma unroll
   for (int j = 0; j < 2; ++j)
     xo[j] = lc0 + 32 * j < tcols ? (lr0 * ldx + (unsigned)(col0 + lc0 + 32 * j)) * 4u : kOob;
+  // the X read: the iterate, or at t = 0 the unscaled X₀ source
+  const bool from0 = s.t == 0;
+  const unsigned ldi = from0 ? (unsigned)P.ld_x0 : ldx;
+  const __amdgpu_buffer_rsrc_t ri =
+      from0 ? range_rsrc(P.x0 + ((int64_t)slice * rows + row0) * ldi, (int64_t)trows * ldi * 4) : rx;
+  unsigned xi[2];
+#pragma unroll
+  for (int j = 0; j < 2; ++j)
+    xi[j] = lc0 + 32 * j < tcols ? (lr0 * ldi + (unsigned)(col0 + lc0 + 32 * j)) * 4u : kOob;
 
   __amdgpu_buffer_rsrc_t rw = rx, ro = rx, rd = rx, rt = rx, rp = rx;
   unsigned wo[2] = {0, 0}, dofs[2] = {0, 0}, tofs[2] = {0, 0}, po[2] = {0, 0};
@@ -892,7 +865,7 @@ __device__ __forceinline__ void apply_epilogue(const DevProblem& P, const Launch
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
       const unsigned rr = (unsigned)(32 * i + 8 * (r >> 2) + (r & 3));
-      xin[slot][r] = buf_ld(rx, xo[j] + rr * ldx * 4u);
+      xin[slot][r] = buf_ld(ri, xi[j] + rr * ldi * 4u);
       if (LAST) win[LAST ? slot : 0][r] = buf_ld(rw, wo[j] + rr * (unsigned)cols * 4u);
     }
   };
@@ -906,7 +879,7 @@ __device__ __forceinline__ void apply_epilogue(const DevProblem& P, const Launch
     const int i = blk >> 1, j = blk & 1;
     float v[16];
 #pragma unroll
-    for (int r = 0; r < 16; ++r) v[r] = fmaf(alpha, xin[slot][r], acc[i][j][r]);
+    for (int r = 0; r < 16; ++r) v[r] = xs * fmaf(alpha, xin[slot][r], acc[i][j][r]);
     if (LAST) {
       float w[16];
 #pragma unroll
@@ -1036,7 +1009,7 @@ __global__ __launch_bounds__(kGemmThreads) void k_gemm(LaunchTable tab, LaunchSc
   }
   float* scal = tab.scal + (int64_t)(P.slice_base + slice) * kScalStride;
 
-  // d_t: at t = 0 from the start kernel; later the sum of the previous apply's
+  // d_t: at t = 0 from the norm kernel; later the sum of the previous apply's
   // per-tile Σ X² partials (fixed order, identical in every workgroup).
   float d;
   if (PH == PH_GRAM && s.t > 0) {
@@ -1047,12 +1020,15 @@ __global__ __launch_bounds__(kGemmThreads) void k_gemm(LaunchTable tab, LaunchSc
     d = scal[1 + s.t];
   }
 
+  // X₀ = inv·B enters through its operands' scale (see the epilogues)
+  const float xs = s.t == 0 && PH != PH_SQUARE ? scal[0] : 1.f;
+
   f32x16_t acc[4][2];
   gemm_mainloop<T>(op, smem, acc);
   if constexpr (PH == PH_APPLY) {
-    apply_epilogue<T, LAST>(P, s, acc, slice, u, row0, col0, d, red);
+    apply_epilogue<T, LAST>(P, s, acc, slice, u, row0, col0, d, xs, red);
   } else {
-    sym_epilogue<T, PH>(P, s, acc, smem, slice, ti, tj, row0, col0, d);
+    sym_epilogue<T, PH>(P, s, acc, smem, slice, ti, tj, row0, col0, d, xs);
   }
 }
 
@@ -1142,10 +1118,9 @@ int launch_phase(int phase, int prec_f32, const LaunchTable& tab, const LaunchSc
   if (e) return e;
   timing_before(phase, stream);
   switch (phase) {
-    case PH_MOMENTUM: hipLaunchKernelGGL(k_momentum, grid, block, 0, st, tab, s); break;
-    case PH_START:
-      if (prec_f32) hipLaunchKernelGGL(k_start<float>, grid, block, 0, st, tab, s);
-      else hipLaunchKernelGGL(k_start<uint16_t>, grid, block, 0, st, tab, s);
+    case PH_INGEST:
+      if (prec_f32) hipLaunchKernelGGL(k_ingest<float>, grid, block, 0, st, tab, s);
+      else hipLaunchKernelGGL(k_ingest<uint16_t>, grid, block, 0, st, tab, s);
       break;
     case PH_GRAM:
       if (prec_f32) hipLaunchKernelGGL((k_gemm<float, PH_GRAM, false>), grid, gblock, kGemmLds, st, tab, s);

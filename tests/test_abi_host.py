@@ -32,7 +32,7 @@ def test_library_exports_every_header_function():
     for name in names:
         assert hasattr(L, name), name
     assert sorted(B.EXPORTED) == names
-    assert L.dmuon_abi_version() == 2 == B.ABI_VERSION
+    assert L.dmuon_abi_version() == 3 == B.ABI_VERSION
 
 
 # --------------------------------------------------------------------------
