@@ -89,12 +89,21 @@ __device__ __forceinline__ int find_prob(const int32_t* prefix, int n, int bid) 
   return lo;
 }
 
-// Σ of a slice's partials in a fixed order.
+// Σ of a slice's partials in a fixed order.  Each thread keeps eight running
+// sums so that eight loads are in flight at once (long lists: one partial per
+// 64×64 tile of a large matrix).
 template <int W>
 __device__ __forceinline__ float sum_partials(const float* part, int count, float* red) {
-  float v = 0.f;
-  for (int i = threadIdx.x; i < count; i += 64 * W) v += part[i];
-  return block_sum<W>(v, red);
+  constexpr int S = 64 * W;
+  float v[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  int i = threadIdx.x;
+  for (; i + 7 * S < count; i += 8 * S) {
+#pragma unroll
+    for (int k = 0; k < 8; ++k) v[k] += part[i + k * S];
+  }
+  for (; i < count; i += S) v[0] += part[i];
+  const float t = ((v[0] + v[1]) + (v[2] + v[3])) + ((v[4] + v[5]) + (v[6] + v[7]));
+  return block_sum<W>(t, red);
 }
 
 // Store 4 consecutive elements of one destination row as one vector (8 bytes of
