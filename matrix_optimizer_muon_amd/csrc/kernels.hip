@@ -786,184 +786,233 @@ typedef unsigned u32x2_t __attribute__((ext_vector_type(2)));
 //        xs = 1
 //   t < k−1: the row-major operand copy, two columns per dword (even lanes take
 //        rows e = 0, 2 from their odd neighbour, odd lanes rows 1, 3), and the
-//        transposed copy, four consecutive rows per store; Σ X'² partial
+//        transposed copy; Σ X'² partial
 //   last:  W ← (1 − lr·wd)·W − lr·X', optional copy of X' to the output.
-// The fp32 loads run ahead of the arithmetic by three blocks (two on the last
-// apply).  All ranges start at the tile's first row (byte offsets then fit in
-// 32 bits); rows past the matrix fall outside them, columns past it get the
-// kOob offset.  Out-of-range rows and columns hold zero in acc (zero-filled
-// operands) and read X as zero, so the zero padding of the operand copies is
-// rewritten with zeros.
+// The bf16 transposed copy is staged in LDS (free once the contraction is done):
+// each lane writes the four consecutive rows it holds of one column as 8 bytes
+// into a 256×256 bf16 tile stored transposed, 8-byte units XOR-swizzled by the
+// column so that 32 lanes writing 32 columns hit distinct banks; after a barrier
+// every thread stores 16-byte pieces of whole transposed rows (512 contiguous
+// bytes per 32 lanes).  Stored directly, each lane would write 8 scattered bytes.
+// The fp32 copy (fp32 path) does not fit in LDS and is stored directly, four
+// rows per 16-byte store.
+// The X (and W) loads run ahead of the arithmetic by three blocks (two on the
+// last apply).  The first kPre blocks are loaded before the contraction starts
+// (prefetch), so their latency hides behind it instead of stalling every
+// workgroup at once when the tiles of a round finish together.  All ranges start
+// at the tile's first row (byte offsets then fit in 32 bits); rows past the
+// matrix fall outside them, columns past it get the kOob offset.  Out-of-range
+// rows and columns hold zero in acc (zero-filled operands) and read X as zero,
+// so the zero padding of the operand copies is rewritten with zeros.
 template <typename T, bool LAST>
-__device__ __forceinline__ void apply_epilogue(const DevProblem& P, const LaunchScalars& s,
-                                               f32x16_t (&acc)[4][2], int slice, int u, int row0,
-                                               int col0, float d, float xs, float* red) {
-  constexpr int kAhead = LAST ? 2 : 3;
-  constexpr unsigned E = sizeof(T);
-  const int lane = threadIdx.x & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int wr = wave >> 2, wc = wave & 3, h = lane >> 5, r32 = lane & 31;
-  const int rows = P.rows, cols = P.cols;
-  const float alpha = s.a + s.b * d + s.c * d * d;
-  const unsigned ldx = (unsigned)P.ld_x;
-  const int trows = rows - row0 < kTile ? rows - row0 : kTile;
-  const int tcols = cols - col0 < kTile ? cols - col0 : kTile;
-  const unsigned lr0 = (unsigned)(wr * 128 + h * 4);   // tile row of register e = 0 (i = rq = 0)
-  const int lc0 = wc * 64 + r32;                        // tile column of block j = 0
-  const bool odd = (lane & 1) != 0;
+struct ApplyEpilogue {
+  static constexpr int kAhead = LAST ? 2 : 3;
+  static constexpr int kPre = LAST ? 1 : 3;       // blocks loaded before the contraction
+  static constexpr unsigned E = sizeof(T);
 
-  const __amdgpu_buffer_rsrc_t rx =
-      range_rsrc(P.xf + ((int64_t)slice * rows + row0) * ldx, (int64_t)trows * ldx * 4);
-  unsigned xo[2];                                       // byte offset of (row lr0, block j)
-#pragma unroll
-  for (int j = 0; j < 2; ++j)
-    xo[j] = lc0 + 32 * j < tcols ? (lr0 * ldx + (unsigned)(col0 + lc0 + 32 * j)) * 4u : kOob;
-  // the X read: the iterate, or at t = 0 the unscaled X₀ source
-  const bool from0 = s.t == 0;
-  const unsigned ldi = from0 ? (unsigned)P.ld_x0 : ldx;
-  const __amdgpu_buffer_rsrc_t ri =
-      from0 ? range_rsrc(P.x0 + ((int64_t)slice * rows + row0) * ldi, (int64_t)trows * ldi * 4) : rx;
-  unsigned xi[2];
-#pragma unroll
-  for (int j = 0; j < 2; ++j)
-    xi[j] = lc0 + 32 * j < tcols ? (lr0 * ldi + (unsigned)(col0 + lc0 + 32 * j)) * 4u : kOob;
+  __amdgpu_buffer_rsrc_t rx, ri, rw, ro, rd, rt, rp;
+  unsigned xo[2], xi[2], wo[2], dofs[2], tofs[2], po[2];
+  unsigned ldx, ldi, ld_s, ld_t, cols;
+  unsigned lr0;
+  int row0;
+  bool odd, pub_pairs;
+  float xin[kAhead][16];
+  float win[LAST ? kAhead : 1][16];
 
-  __amdgpu_buffer_rsrc_t rw = rx, ro = rx, rd = rx, rt = rx, rp = rx;
-  unsigned wo[2] = {0, 0}, dofs[2] = {0, 0}, tofs[2] = {0, 0}, po[2] = {0, 0};
-  unsigned ld_s = 0, ld_t = 0;
-  // published bf16 copy: two columns per dword when rows hold an even number of
-  // columns (a pair never straddles rows), else one 16-bit store per element
-  const bool pub_pairs = (cols & 1) == 0;
-  if (LAST) {
-    const int64_t first = ((int64_t)slice * rows + row0) * cols, bytes = (int64_t)trows * cols * 4;
-    rw = range_rsrc(s.write_master ? P.master + first : nullptr, bytes);
-    ro = range_rsrc(P.out ? P.out + first : nullptr, bytes);
-    rp = range_rsrc(s.write_master && P.pub ? P.pub + first : nullptr, (int64_t)trows * cols * 2);
+  __device__ __forceinline__ ApplyEpilogue(const DevProblem& P, const LaunchScalars& s, int slice, int row0_,
+                                           int col0) {
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int wr = wave >> 2, wc = wave & 3, h = lane >> 5, r32 = lane & 31;
+    const int rows = P.rows;
+    row0 = row0_;
+    cols = (unsigned)P.cols;
+    ldx = (unsigned)P.ld_x;
+    const int trows = rows - row0 < kTile ? rows - row0 : kTile;
+    const int tcols = P.cols - col0 < kTile ? P.cols - col0 : kTile;
+    lr0 = (unsigned)(wr * 128 + h * 4);                 // tile row of register e = 0 (i = rq = 0)
+    const int lc0 = wc * 64 + r32;                      // tile column of block j = 0
+    odd = (lane & 1) != 0;
+
+    rx = range_rsrc(P.xf + ((int64_t)slice * rows + row0) * ldx, (int64_t)trows * ldx * 4);
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      wo[j] = lc0 + 32 * j < tcols ? (lr0 * (unsigned)cols + (unsigned)(col0 + lc0 + 32 * j)) * 4u : kOob;
-      const unsigned gc = (unsigned)(col0 + lc0 + 32 * j);
-      po[j] = lc0 + 32 * j < tcols
-                  ? (pub_pairs ? ((lr0 + (odd ? 1u : 0u)) * (unsigned)cols + (gc & ~1u)) * 2u
-                               : (lr0 * (unsigned)cols + gc) * 2u)
-                  : kOob;
-    }
-  } else {
-    ld_s = (unsigned)(P.wide ? P.ld_n : P.ld_m);
-    ld_t = (unsigned)(P.wide ? P.ld_m : P.ld_n);
-    void* xa_next = (s.t & 1) ? P.xa0 : P.xa1;
-    const T* dst = (const T*)(P.wide ? P.xg : xa_next) + (int64_t)slice * rows * ld_s;
-    const T* dstT = (const T*)(P.wide ? xa_next : P.xg) + (int64_t)slice * cols * ld_t;
-    rd = range_rsrc(dst + (int64_t)row0 * ld_s, (int64_t)trows * ld_s * E);
-    rt = range_rsrc(dstT + (int64_t)col0 * ld_t, (int64_t)tcols * ld_t * E);
+    for (int j = 0; j < 2; ++j)
+      xo[j] = lc0 + 32 * j < tcols ? (lr0 * ldx + (unsigned)(col0 + lc0 + 32 * j)) * 4u : kOob;
+    // the X read: the iterate, or at t = 0 the unscaled X₀ source
+    const bool from0 = s.t == 0;
+    ldi = from0 ? (unsigned)P.ld_x0 : ldx;
+    ri = from0 ? range_rsrc(P.x0 + ((int64_t)slice * rows + row0) * ldi, (int64_t)trows * ldi * 4) : rx;
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      // row-major copy: the lane's dword starts at an even column
-      const unsigned gc = (unsigned)(col0 + lc0 + 32 * j);
-      const unsigned gce = E == 2 ? (gc & ~1u) : gc;
-      dofs[j] = gce < ld_s ? ((lr0 + (E == 2 && odd ? 1u : 0u)) * ld_s + gce) * E : kOob;
-      // transposed copy: row (lc0 + 32 j) of the range, columns from row0 + lr0
-      tofs[j] = ((unsigned)(lc0 + 32 * j) * ld_t + (unsigned)row0 + lr0) * E;
+    for (int j = 0; j < 2; ++j)
+      xi[j] = lc0 + 32 * j < tcols ? (lr0 * ldi + (unsigned)(col0 + lc0 + 32 * j)) * 4u : kOob;
+
+    rw = ro = rd = rt = rp = rx;
+    ld_s = ld_t = 0;
+#pragma unroll
+    for (int j = 0; j < 2; ++j) wo[j] = dofs[j] = tofs[j] = po[j] = 0;
+    // published bf16 copy: two columns per dword when rows hold an even number of
+    // columns (a pair never straddles rows), else one 16-bit store per element
+    pub_pairs = (P.cols & 1) == 0;
+    if (LAST) {
+      const int64_t first = ((int64_t)slice * rows + row0) * P.cols, bytes = (int64_t)trows * P.cols * 4;
+      rw = range_rsrc(s.write_master ? P.master + first : nullptr, bytes);
+      ro = range_rsrc(P.out ? P.out + first : nullptr, bytes);
+      rp = range_rsrc(s.write_master && P.pub ? P.pub + first : nullptr, (int64_t)trows * P.cols * 2);
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        wo[j] = lc0 + 32 * j < tcols ? (lr0 * cols + (unsigned)(col0 + lc0 + 32 * j)) * 4u : kOob;
+        const unsigned gc = (unsigned)(col0 + lc0 + 32 * j);
+        po[j] = lc0 + 32 * j < tcols
+                    ? (pub_pairs ? ((lr0 + (odd ? 1u : 0u)) * cols + (gc & ~1u)) * 2u : (lr0 * cols + gc) * 2u)
+                    : kOob;
+      }
+    } else {
+      ld_s = (unsigned)(P.wide ? P.ld_n : P.ld_m);
+      ld_t = (unsigned)(P.wide ? P.ld_m : P.ld_n);
+      void* xa_next = (s.t & 1) ? P.xa0 : P.xa1;
+      const T* dst = (const T*)(P.wide ? P.xg : xa_next) + (int64_t)slice * rows * ld_s;
+      const T* dstT = (const T*)(P.wide ? xa_next : P.xg) + (int64_t)slice * P.cols * ld_t;
+      rd = range_rsrc(dst + (int64_t)row0 * ld_s, (int64_t)trows * ld_s * E);
+      rt = range_rsrc(dstT + (int64_t)col0 * ld_t, (int64_t)tcols * ld_t * E);
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        // row-major copy: the lane's dword starts at an even column
+        const unsigned gc = (unsigned)(col0 + lc0 + 32 * j);
+        const unsigned gce = E == 2 ? (gc & ~1u) : gc;
+        dofs[j] = gce < ld_s ? ((lr0 + (E == 2 && odd ? 1u : 0u)) * ld_s + gce) * E : kOob;
+        // transposed copy: row (lc0 + 32 j) of the range, columns from row0 + lr0
+        tofs[j] = ((unsigned)(lc0 + 32 * j) * ld_t + (unsigned)row0 + lr0) * E;
+      }
     }
   }
 
-  float xin[kAhead][16];
-  float win[LAST ? kAhead : 1][16];
-  auto load_blk = [&](int blk, int slot) {
+  __device__ __forceinline__ void load_blk(int blk, int slot) {
     const int i = blk >> 1, j = blk & 1;
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
       const unsigned rr = (unsigned)(32 * i + 8 * (r >> 2) + (r & 3));
       xin[slot][r] = buf_ld(ri, xi[j] + rr * ldi * 4u);
-      if (LAST) win[LAST ? slot : 0][r] = buf_ld(rw, wo[j] + rr * (unsigned)cols * 4u);
+      if (LAST) win[LAST ? slot : 0][r] = buf_ld(rw, wo[j] + rr * cols * 4u);
     }
-  };
+  }
 
-  float sq = 0.f;
+  __device__ __forceinline__ void prefetch() {
 #pragma unroll
-  for (int b = 0; b < kAhead; ++b) load_blk(b, b);
+    for (int b = 0; b < kPre; ++b) load_blk(b, b);
+  }
+
+  // byte offset in the LDS-staged transposed tile of the 8-byte unit that holds
+  // tile rows 4·unit .. 4·unit + 3 of tile column c
+  static __device__ __forceinline__ unsigned t_stage_off(unsigned c, unsigned unit) {
+    return c * 512u + ((unit ^ (c & 31u)) << 3);
+  }
+
+  __device__ __forceinline__ void finish(const DevProblem& P, const LaunchScalars& s, f32x16_t (&acc)[4][2],
+                                         int slice, int u, float d, float xs, char* smem, float* red) {
+    constexpr bool kStageT = E == 2 && !LAST;
+    const unsigned lc0 = (unsigned)(((threadIdx.x >> 6) & 3) * 64 + (threadIdx.x & 31));
+    const float alpha = s.a + s.b * d + s.c * d * d;
+    float sq = 0.f;
 #pragma unroll
-  for (int blk = 0; blk < 8; ++blk) {
-    const int slot = blk % kAhead;
-    const int i = blk >> 1, j = blk & 1;
-    float v[16];
+    for (int b = kPre; b < kAhead; ++b) load_blk(b, b);
 #pragma unroll
-    for (int r = 0; r < 16; ++r) v[r] = xs * fmaf(alpha, xin[slot][r], acc[i][j][r]);
-    if (LAST) {
-      float w[16];
+    for (int blk = 0; blk < 8; ++blk) {
+      const int slot = blk % kAhead;
+      const int i = blk >> 1, j = blk & 1;
+      float v[16];
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const unsigned rr = (unsigned)(32 * i + 8 * (r >> 2) + (r & 3));
-        const unsigned o = wo[j] + rr * (unsigned)cols * 4u;
-        w[r] = fmaf(-s.lr, v[r], s.decay * win[LAST ? slot : 0][r]);
-        buf_st(ro, o, v[r]);
-        buf_st(rw, o, w[r]);
-      }
-      if (pub_pairs) {
+      for (int r = 0; r < 16; ++r) v[r] = xs * fmaf(alpha, xin[slot][r], acc[i][j][r]);
+      if (LAST) {
+        float w[16];
 #pragma unroll
-        for (int rq = 0; rq < 4; ++rq)
+        for (int r = 0; r < 16; ++r) {
+          const unsigned rr = (unsigned)(32 * i + 8 * (r >> 2) + (r & 3));
+          const unsigned o = wo[j] + rr * cols * 4u;
+          w[r] = fmaf(-s.lr, v[r], s.decay * win[LAST ? slot : 0][r]);
+          buf_st(ro, o, v[r]);
+          buf_st(rw, o, w[r]);
+        }
+        if (pub_pairs) {
 #pragma unroll
-          for (int pe = 0; pe < 2; ++pe) {
-            const float w0 = w[4 * rq + 2 * pe], w1 = w[4 * rq + 2 * pe + 1];
-            const float got = swap_adjacent(odd ? w0 : w1);
-            const unsigned rr = (unsigned)(32 * i + 8 * rq + 2 * pe);
-            buf_st(rp, po[j] + rr * (unsigned)cols * 2u, odd ? pack_bf16x2(got, w1) : pack_bf16x2(w0, got));
+          for (int rq = 0; rq < 4; ++rq)
+#pragma unroll
+            for (int pe = 0; pe < 2; ++pe) {
+              const float w0 = w[4 * rq + 2 * pe], w1 = w[4 * rq + 2 * pe + 1];
+              const float got = swap_adjacent(odd ? w0 : w1);
+              const unsigned rr = (unsigned)(32 * i + 8 * rq + 2 * pe);
+              buf_st(rp, po[j] + rr * cols * 2u, odd ? pack_bf16x2(got, w1) : pack_bf16x2(w0, got));
+            }
+        } else {
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const unsigned rr = (unsigned)(32 * i + 8 * (r >> 2) + (r & 3));
+            __builtin_amdgcn_raw_buffer_store_b16(f32_to_bf16(w[r]), rp, (int)(po[j] + rr * cols * 2u), 0, 0);
           }
+        }
       } else {
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const unsigned rr = (unsigned)(32 * i + 8 * (r >> 2) + (r & 3));
-          __builtin_amdgcn_raw_buffer_store_b16(f32_to_bf16(w[r]), rp, (int)(po[j] + rr * (unsigned)cols * 2u), 0, 0);
+          buf_st(rx, xo[j] + rr * ldx * 4u, v[r]);
+          sq = fmaf(v[r], v[r], sq);
         }
-      }
-    } else {
+        // transposed copy: four consecutive rows of one column
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const unsigned rr = (unsigned)(32 * i + 8 * (r >> 2) + (r & 3));
-        buf_st(rx, xo[j] + rr * ldx * 4u, v[r]);
-        sq = fmaf(v[r], v[r], sq);
-      }
-      // transposed copy: four consecutive rows of one column per store
-#pragma unroll
-      for (int rq = 0; rq < 4; ++rq) {
-        const unsigned rr = (unsigned)(32 * i + 8 * rq);
-        const unsigned o = (unsigned)row0 + lr0 + rr < ld_t ? tofs[j] + rr * E : kOob;
-        if constexpr (E == 2) {
-          const u32x2_t w2 = {pack_bf16x2(v[4 * rq], v[4 * rq + 1]), pack_bf16x2(v[4 * rq + 2], v[4 * rq + 3])};
-          __builtin_amdgcn_raw_buffer_store_b64(w2, rt, (int)o, 0, 0);
-        } else {
-          const u32x4_t w4 = {__float_as_uint(v[4 * rq]), __float_as_uint(v[4 * rq + 1]),
-                              __float_as_uint(v[4 * rq + 2]), __float_as_uint(v[4 * rq + 3])};
-          __builtin_amdgcn_raw_buffer_store_b128(w4, rt, (int)o, 0, 0);
-        }
-      }
-      // row-major copy
-#pragma unroll
-      for (int rq = 0; rq < 4; ++rq) {
-        if constexpr (E == 2) {
-#pragma unroll
-          for (int pe = 0; pe < 2; ++pe) {        // register pair (2pe, 2pe + 1)
-            const float v0 = v[4 * rq + 2 * pe], v1 = v[4 * rq + 2 * pe + 1];
-            const float got = swap_adjacent(odd ? v0 : v1);
-            const unsigned rr = (unsigned)(32 * i + 8 * rq + 2 * pe);
-            buf_st(rd, dofs[j] + rr * ld_s * E, odd ? pack_bf16x2(got, v1) : pack_bf16x2(v0, got));
-          }
-        } else {
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const unsigned rr = (unsigned)(32 * i + 8 * rq + e);
-            buf_st(rd, dofs[j] + rr * ld_s * E, v[4 * rq + e]);
+        for (int rq = 0; rq < 4; ++rq) {
+          const unsigned rr = (unsigned)(32 * i + 8 * rq);
+          if constexpr (kStageT) {
+            const u32x2_t w2 = {pack_bf16x2(v[4 * rq], v[4 * rq + 1]), pack_bf16x2(v[4 * rq + 2], v[4 * rq + 3])};
+            *(__attribute__((address_space(3))) u32x2_t*)(smem + t_stage_off(lc0 + 32u * j, (lr0 + rr) >> 2)) = w2;
+          } else {
+            const unsigned o = (unsigned)row0 + lr0 + rr < ld_t ? tofs[j] + rr * E : kOob;
+            const u32x4_t w4 = {__float_as_uint(v[4 * rq]), __float_as_uint(v[4 * rq + 1]),
+                                __float_as_uint(v[4 * rq + 2]), __float_as_uint(v[4 * rq + 3])};
+            __builtin_amdgcn_raw_buffer_store_b128(w4, rt, (int)o, 0, 0);
           }
         }
+        // row-major copy
+#pragma unroll
+        for (int rq = 0; rq < 4; ++rq) {
+          if constexpr (E == 2) {
+#pragma unroll
+            for (int pe = 0; pe < 2; ++pe) {        // register pair (2pe, 2pe + 1)
+              const float v0 = v[4 * rq + 2 * pe], v1 = v[4 * rq + 2 * pe + 1];
+              const float got = swap_adjacent(odd ? v0 : v1);
+              const unsigned rr = (unsigned)(32 * i + 8 * rq + 2 * pe);
+              buf_st(rd, dofs[j] + rr * ld_s * E, odd ? pack_bf16x2(got, v1) : pack_bf16x2(v0, got));
+            }
+          } else {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              const unsigned rr = (unsigned)(32 * i + 8 * rq + e);
+              buf_st(rd, dofs[j] + rr * ld_s * E, v[4 * rq + e]);
+            }
+          }
+        }
+      }
+      if (blk + kAhead < 8) load_blk(blk + kAhead, slot);
+    }
+    if (!LAST) {
+      // (the barriers of the sum also publish the staged transposed tile)
+      const float tot = block_sum<kGemmWaves>(sq, red);
+      if (threadIdx.x == 0) P.part_apply[(int64_t)slice * P.apply_tr * P.apply_tc + u] = tot;
+    }
+    if constexpr (kStageT) {
+      // 256 transposed rows × 32 pieces of 16 bytes (tile rows 8q .. 8q + 7)
+#pragma unroll 4
+      for (int k = 0; k < 16; ++k) {
+        const unsigned id = threadIdx.x + (unsigned)kGemmThreads * k;
+        const unsigned c = id >> 5, q = id & 31;
+        const unsigned sw = c & 31u;
+        // logical units 2q, 2q + 1 sit at 2(q ^ sw/2) + (sw & 1) and its neighbour
+        u32x4_t p = *(const __attribute__((address_space(3))) u32x4_t*)(smem + c * 512u + ((q ^ (sw >> 1)) << 4));
+        if (sw & 1u) p = u32x4_t{p.z, p.w, p.x, p.y};
+        const unsigned o = (unsigned)row0 + 8u * q < ld_t ? (c * ld_t + (unsigned)row0 + 8u * q) * 2u : kOob;
+        __builtin_amdgcn_raw_buffer_store_b128(p, rt, (int)o, 0, 0);
       }
     }
-    if (blk + kAhead < 8) load_blk(blk + kAhead, slot);
   }
-  if (!LAST) {
-    const float tot = block_sum<kGemmWaves>(sq, red);
-    if (threadIdx.x == 0) P.part_apply[(int64_t)slice * P.apply_tr * P.apply_tc + u] = tot;
-  }
-}
+};
 
 template <typename T, int PH, bool LAST>
 __global__ __launch_bounds__(kGemmThreads) void k_gemm(LaunchTable tab, LaunchScalars s) {
@@ -1033,10 +1082,13 @@ __global__ __launch_bounds__(kGemmThreads) void k_gemm(LaunchTable tab, LaunchSc
   const float xs = s.t == 0 && PH != PH_SQUARE ? scal[0] : 1.f;
 
   f32x16_t acc[4][2];
-  gemm_mainloop<T>(op, smem, acc);
   if constexpr (PH == PH_APPLY) {
-    apply_epilogue<T, LAST>(P, s, acc, slice, u, row0, col0, d, xs, red);
+    ApplyEpilogue<T, LAST> epi(P, s, slice, row0, col0);
+    epi.prefetch();
+    gemm_mainloop<T>(op, smem, acc);
+    epi.finish(P, s, acc, slice, u, d, xs, smem, red);
   } else {
+    gemm_mainloop<T>(op, smem, acc);
     sym_epilogue<T, PH>(P, s, acc, smem, slice, ti, tj, row0, col0, d, xs);
   }
 }
