@@ -199,14 +199,15 @@ static int build_plan(const std::vector<Item>& items, int prec_f32, Plan& pl, ch
     P.pub = it.pub;
     const int64_t b = it.batch;
     const int64_t prep = (int64_t)P.prep_tiles_r * P.prep_tiles_c;
-    P.xf = (float*)carve((size_t)(b * it.rows * P.ld_x) * 4);
+    P.xf = (float*)carve((size_t)(b * P.apply_tr * P.apply_tc) * kTile * kTile * 4);
+    if (!it.mom) P.xraw = (float*)carve((size_t)(b * it.rows * P.ld_x) * 4);
     P.xg = carve((size_t)(b * P.m * P.ld_n) * esz);
     P.xa0 = carve((size_t)(b * P.n * P.ld_m) * esz);
     P.xa1 = carve((size_t)(b * P.n * P.ld_m) * esz);
     P.ap = carve((size_t)(b * P.m * P.ld_m) * esz);
     P.bp = carve((size_t)(b * P.m * P.ld_m) * esz);
     P.part_norm = (float*)carve((size_t)(b * prep) * 4);
-    P.x0 = it.mom ? it.mom : P.xf;
+    P.x0 = it.mom ? it.mom : P.xraw;
     P.ld_x0 = it.mom ? (int32_t)it.cols : P.ld_x;
     P.part_apply = (float*)carve((size_t)(b * P.apply_tr * P.apply_tc) * 4);
     const int64_t tri = (int64_t)P.tiles_m * (P.tiles_m + 1) / 2;

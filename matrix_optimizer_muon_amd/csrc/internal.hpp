@@ -44,7 +44,7 @@ struct DevProblem {
   int32_t tiles_m;             // ceil(m / 256)
   int32_t apply_tr, apply_tc;  // apply tiles per slice over rows / cols of storage
   int32_t slice_base;          // global index of this problem's first slice
-  int32_t ld_x;                // round_up(cols, 32): ld of the fp32 iterate
+  int32_t ld_x;                // round_up(cols, 32): ld of xraw
   // per-phase workgroup prefix (first global workgroup of this problem)
   int32_t wg0[PH_COUNT];
   int32_t ld_x0;               // ld of x0
@@ -55,9 +55,12 @@ struct DevProblem {
   float* out;                  // NS output (NULL if not wanted)
   uint16_t* pub;               // bf16 published parameter (NULL if not wanted)
   const float* x0;             // X₀ before its 1/(‖B‖_F + eps) scale: the momentum
-                               // (ld cols), or for ns_batched x in the iterate buffer
+                               // (ld cols), or for ns_batched xraw (ld ld_x)
   // workspace (operand element type = bf16 or fp32 per precision)
-  float* xf;                   // fp32 iterate, storage layout rows×ld_x, stride rows*ld_x
+  float* xf;                   // fp32 iterate in the apply's register order: per 256×256
+                               // tile (row-major tile order) kTile² floats laid out as
+                               // [wave 8][block 8][quad rq 4][lane 64][4 rows]
+  float* xraw;                 // ns_batched only: x in fp32, storage layout rows×ld_x
   void* xg;                    // oriented X, m×ld_n, stride m*ld_n
   void* xa0;                   // oriented Xᵀ, n×ld_m, stride n*ld_m (ping)
   void* xa1;                   // (pong)

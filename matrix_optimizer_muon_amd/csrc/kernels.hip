@@ -195,7 +195,7 @@ __global__ __launch_bounds__(kThreads) void k_ingest(LaunchTable tab, LaunchScal
   const uint16_t* gb = (const uint16_t*)P.grad + (int64_t)slice * per;
   const float* gf = (const float*)P.grad + (int64_t)slice * per;
   float* mom = s.has_momentum ? P.mom + (int64_t)slice * per : nullptr;
-  float* xf = s.has_momentum ? nullptr : P.xf + (int64_t)slice * rows * P.ld_x;
+  float* xf = s.has_momentum ? nullptr : P.xraw + (int64_t)slice * rows * P.ld_x;
   const int ld_s = P.wide ? P.ld_n : P.ld_m;    // straight copy: cols padded
   const int ld_t = P.wide ? P.ld_m : P.ld_n;    // transposed copy: rows padded
   T* cs = (T*)(P.wide ? P.xg : P.xa0) + (int64_t)slice * rows * ld_s;
@@ -780,10 +780,12 @@ typedef unsigned u32x2_t __attribute__((ext_vector_type(2)));
 // Lane (h, r32) of wave (wr, wc) holds, for block (i, j) and register r = 4·rq + e,
 // the element at tile row 128·wr + 32·i + 8·rq + 4·h + e and tile column
 // 64·wc + 32·j + r32.  Per block:
-//   X' = xs·(α·X + acc) (fp32 iterate, read and written with 4-byte accesses:
-//        each wave instruction covers two 128-byte row segments), α = a + b·d + c·d²;
-//        at t = 0 X is read from the unscaled source x0 (B) and xs = inv, else
-//        xs = 1
+//   X' = xs·(α·X + acc), α = a + b·d + c·d²; at t = 0 X is read from the
+//        unscaled source x0 (B, storage layout, 4-byte accesses: each wave
+//        instruction covers two 128-byte row segments) and xs = inv, else xs = 1
+//        and X is the fp32 iterate, which is kept in the order of the registers
+//        (one 16-byte piece per lane and quad rq, 1 KiB contiguous per wave
+//        instruction), so it moves with 4 loads and 4 stores per block
 //   t < k−1: the row-major operand copy, two columns per dword (even lanes take
 //        rows e = 0, 2 from their odd neighbour, odd lanes rows 1, 3), and the
 //        transposed copy; Σ X'² partial
@@ -811,37 +813,36 @@ struct ApplyEpilogue {
   static constexpr unsigned E = sizeof(T);
 
   __amdgpu_buffer_rsrc_t rx, ri, rw, ro, rd, rt, rp;
-  unsigned xo[2], xi[2], wo[2], dofs[2], tofs[2], po[2];
-  unsigned ldx, ldi, ld_s, ld_t, cols;
+  unsigned xi[2], wo[2], dofs[2], tofs[2], po[2];
+  unsigned xb, ldi, ld_s, ld_t, cols;
   unsigned lr0;
   int row0;
-  bool odd, pub_pairs;
+  bool odd, pub_pairs, from0;
   float xin[kAhead][16];
   float win[LAST ? kAhead : 1][16];
 
-  __device__ __forceinline__ ApplyEpilogue(const DevProblem& P, const LaunchScalars& s, int slice, int row0_,
-                                           int col0) {
+  __device__ __forceinline__ ApplyEpilogue(const DevProblem& P, const LaunchScalars& s, int slice, int u,
+                                           int row0_, int col0) {
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int wr = wave >> 2, wc = wave & 3, h = lane >> 5, r32 = lane & 31;
     const int rows = P.rows;
     row0 = row0_;
     cols = (unsigned)P.cols;
-    ldx = (unsigned)P.ld_x;
     const int trows = rows - row0 < kTile ? rows - row0 : kTile;
     const int tcols = P.cols - col0 < kTile ? P.cols - col0 : kTile;
     lr0 = (unsigned)(wr * 128 + h * 4);                 // tile row of register e = 0 (i = rq = 0)
     const int lc0 = wc * 64 + r32;                      // tile column of block j = 0
     odd = (lane & 1) != 0;
 
-    rx = range_rsrc(P.xf + ((int64_t)slice * rows + row0) * ldx, (int64_t)trows * ldx * 4);
-#pragma unroll
-    for (int j = 0; j < 2; ++j)
-      xo[j] = lc0 + 32 * j < tcols ? (lr0 * ldx + (unsigned)(col0 + lc0 + 32 * j)) * 4u : kOob;
-    // the X read: the iterate, or at t = 0 the unscaled X₀ source
-    const bool from0 = s.t == 0;
-    ldi = from0 ? (unsigned)P.ld_x0 : ldx;
-    ri = from0 ? range_rsrc(P.x0 + ((int64_t)slice * rows + row0) * ldi, (int64_t)trows * ldi * 4) : rx;
+    // the iterate's tile: byte (((wave·8 + blk)·4 + rq)·64 + lane)·16
+    rx = range_rsrc(P.xf + ((int64_t)slice * P.apply_tr * P.apply_tc + u) * (kTile * kTile),
+                    (int64_t)kTile * kTile * 4);
+    xb = (unsigned)((wave * 8 * 4 * 64 + lane) * 16);
+    // the X₀ read at t = 0: the unscaled source in storage layout
+    from0 = s.t == 0;
+    ldi = (unsigned)P.ld_x0;
+    ri = range_rsrc(from0 ? P.x0 + ((int64_t)slice * rows + row0) * ldi : nullptr, (int64_t)trows * ldi * 4);
 #pragma unroll
     for (int j = 0; j < 2; ++j)
       xi[j] = lc0 + 32 * j < tcols ? (lr0 * ldi + (unsigned)(col0 + lc0 + 32 * j)) * 4u : kOob;
@@ -886,13 +887,33 @@ struct ApplyEpilogue {
     }
   }
 
+  // byte offset of quad rq of block blk in the iterate's tile
+  __device__ __forceinline__ unsigned xq(int blk, int rq) const {
+    return xb + (unsigned)((blk * 4 + rq) * 64 * 16);
+  }
+
   __device__ __forceinline__ void load_blk(int blk, int slot) {
     const int i = blk >> 1, j = blk & 1;
+    if (from0) {
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const unsigned rr = (unsigned)(32 * i + 8 * (r >> 2) + (r & 3));
-      xin[slot][r] = buf_ld(ri, xi[j] + rr * ldi * 4u);
-      if (LAST) win[LAST ? slot : 0][r] = buf_ld(rw, wo[j] + rr * cols * 4u);
+      for (int r = 0; r < 16; ++r) {
+        const unsigned rr = (unsigned)(32 * i + 8 * (r >> 2) + (r & 3));
+        xin[slot][r] = buf_ld(ri, xi[j] + rr * ldi * 4u);
+      }
+    } else {
+#pragma unroll
+      for (int rq = 0; rq < 4; ++rq) {
+        const f32x4_t q = __builtin_amdgcn_raw_buffer_load_b128(rx, (int)xq(blk, rq), 0, 0);
+        xin[slot][4 * rq] = q.x; xin[slot][4 * rq + 1] = q.y;
+        xin[slot][4 * rq + 2] = q.z; xin[slot][4 * rq + 3] = q.w;
+      }
+    }
+    if (LAST) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const unsigned rr = (unsigned)(32 * i + 8 * (r >> 2) + (r & 3));
+        win[LAST ? slot : 0][r] = buf_ld(rw, wo[j] + rr * cols * 4u);
+      }
     }
   }
 
@@ -951,11 +972,11 @@ struct ApplyEpilogue {
         }
       } else {
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const unsigned rr = (unsigned)(32 * i + 8 * (r >> 2) + (r & 3));
-          buf_st(rx, xo[j] + rr * ldx * 4u, v[r]);
-          sq = fmaf(v[r], v[r], sq);
-        }
+        for (int r = 0; r < 16; ++r) sq = fmaf(v[r], v[r], sq);
+#pragma unroll
+        for (int rq = 0; rq < 4; ++rq)
+          __builtin_amdgcn_raw_buffer_store_b128(
+              f32x4_t{v[4 * rq], v[4 * rq + 1], v[4 * rq + 2], v[4 * rq + 3]}, rx, (int)xq(blk, rq), 0, 0);
         // transposed copy: four consecutive rows of one column
 #pragma unroll
         for (int rq = 0; rq < 4; ++rq) {
@@ -1083,7 +1104,7 @@ __global__ __launch_bounds__(kGemmThreads) void k_gemm(LaunchTable tab, LaunchSc
 
   f32x16_t acc[4][2];
   if constexpr (PH == PH_APPLY) {
-    ApplyEpilogue<T, LAST> epi(P, s, slice, row0, col0);
+    ApplyEpilogue<T, LAST> epi(P, s, slice, u, row0, col0);
     epi.prefetch();
     gemm_mainloop<T>(op, smem, acc);
     epi.finish(P, s, acc, slice, u, d, xs, smem, red);
