@@ -613,12 +613,51 @@ __device__ __forceinline__ int acc_col(int j) {
   return (wave & 3) * 64 + j * 32 + (lane & 31);
 }
 
-// upper-triangle tile u (row-major over ti ≤ tj) of a T×T tile grid
+// Tile orders.  Consecutive logical tiles run on one XCD in runs of kXcdRun (see
+// xcd_logical_block), so the order decides how many operand panels one XCD's L2
+// has to hold at once.  Both orders walk bands of kBand tiles along one side of
+// the output and advance the other side every kBand tiles, so a run of 32 tiles
+// covers about 8 × 4 tiles and touches ~12 panels (a row-by-row order touched
+// ~33: for an 8192 × 28672 matrix, all 32 panels of B' per XCD and round).
+constexpr int kBand = 8;
+
+// apply: R tiles along the short side, C along the long one; returns the
+// short-side and long-side tile indices of logical tile u
+__device__ __forceinline__ void band_tile(int u, int R, int C, int& ts, int& tl) {
+  const int b = u / (kBand * C);
+  const int r0 = b * kBand;
+  const int gb = R - r0 < kBand ? R - r0 : kBand;
+  const int v = u - b * kBand * C;
+  ts = r0 + v % gb;
+  tl = v / gb;
+}
+
+// Gram / square: upper-triangle tile u (ti ≤ tj) of a T×T grid.  Band b holds
+// rows [8b, 8b + h): first its triangle (tj from 8b to 8b + h − 1, each with
+// the rows up to tj), then h rows for every later tj.
 __device__ __forceinline__ void tri_tile(int u, int T, int& ti, int& tj) {
-  int i = 0, start = 0;
-  while (start + (T - i) <= u) { start += T - i; ++i; }
-  ti = i;
-  tj = i + (u - start);
+  int r0 = 0, start = 0;
+  for (;;) {
+    const int h = T - r0 < kBand ? T - r0 : kBand;
+    const int n = h * (h + 1) / 2 + h * (T - r0 - h);
+    if (u < start + n) {
+      int v = u - start;
+      const int tri = h * (h + 1) / 2;
+      if (v < tri) {
+        int k = 0;
+        while ((k + 1) * (k + 2) / 2 <= v) ++k;
+        ti = r0 + (v - k * (k + 1) / 2);
+        tj = r0 + k;
+      } else {
+        v -= tri;
+        ti = r0 + v % h;
+        tj = r0 + h + v / h;
+      }
+      return;
+    }
+    start += n;
+    r0 += kBand;
+  }
 }
 
 // Logical workgroup index.  Workgroups are handed to the 8 XCDs round-robin in
@@ -1065,13 +1104,13 @@ __global__ __launch_bounds__(kGemmThreads) void k_gemm(LaunchTable tab, LaunchSc
     op.rows_a = m - row0;
     op.rows_b = m - col0;
     op.ktiles = ld / kElemsPerRow;
-  } else {  // PH_APPLY: tiles ordered with the long (n) dimension outermost
+  } else {  // PH_APPLY: bands along the short (m) side, see band_tile
     const int per = P.apply_tr * P.apply_tc;
     slice = local / per;
     u = local % per;
     int tr, tc;
-    if (P.wide) { tc = u / P.apply_tr; tr = u % P.apply_tr; }
-    else { tr = u / P.apply_tc; tc = u % P.apply_tc; }
+    if (P.wide) band_tile(u, P.apply_tr, P.apply_tc, tr, tc);
+    else band_tile(u, P.apply_tc, P.apply_tr, tc, tr);
     u = tr * P.apply_tc + tc;           // partial-sum slot in row-major tile order
     row0 = tr * kTile;
     col0 = tc * kTile;
