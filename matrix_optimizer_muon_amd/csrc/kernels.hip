@@ -855,18 +855,19 @@ struct ApplyEpilogue {
   unsigned xi[2], wo[2], dofs[2], tofs[2], po[2];
   unsigned xb, ldi, ld_s, ld_t, cols;
   unsigned lr0;
-  int row0;
+  int row0, col0;
   bool odd, pub_pairs, from0;
   float xin[kAhead][16];
   float win[LAST ? kAhead : 1][16];
 
   __device__ __forceinline__ ApplyEpilogue(const DevProblem& P, const LaunchScalars& s, int slice, int u,
-                                           int row0_, int col0) {
+                                           int row0_, int col0_) {
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int wr = wave >> 2, wc = wave & 3, h = lane >> 5, r32 = lane & 31;
     const int rows = P.rows;
     row0 = row0_;
+    col0 = col0_;
     cols = (unsigned)P.cols;
     const int trows = rows - row0 < kTile ? rows - row0 : kTile;
     const int tcols = P.cols - col0 < kTile ? P.cols - col0 : kTile;
@@ -961,6 +962,13 @@ struct ApplyEpilogue {
     for (int b = 0; b < kPre; ++b) load_blk(b, b);
   }
 
+  // 16-byte-piece swizzle of the LDS-staged row-major tile: the four rows one
+  // dword store instruction writes (r, r + 1, r + 4, r + 5 for r ≡ 0 or 2 mod 8)
+  // land in four different bank quarters
+  static __device__ __forceinline__ unsigned row_swz(unsigned r) {
+    return ((r & 1u) | ((r >> 1) & 2u)) << 2;
+  }
+
   // byte offset in the LDS-staged transposed tile of the 8-byte unit that holds
   // tile rows 4·unit .. 4·unit + 3 of tile column c
   static __device__ __forceinline__ unsigned t_stage_off(unsigned c, unsigned unit) {
@@ -970,6 +978,9 @@ struct ApplyEpilogue {
   __device__ __forceinline__ void finish(const DevProblem& P, const LaunchScalars& s, f32x16_t (&acc)[4][2],
                                          int slice, int u, float d, float xs, char* smem, float* red) {
     constexpr bool kStageT = E == 2 && !LAST;
+    // bf16 row-major copy, staged after the transposed one: the dword each lane
+    // would store per block and (quad rq, pair pe), kept until LDS is free again
+    uint32_t keep[kStageT ? 8 : 1][8];
     const unsigned lc0 = (unsigned)(((threadIdx.x >> 6) & 3) * 64 + (threadIdx.x & 31));
     const float alpha = s.a + s.b * d + s.c * d * d;
     float sq = 0.f;
@@ -1038,8 +1049,7 @@ struct ApplyEpilogue {
             for (int pe = 0; pe < 2; ++pe) {        // register pair (2pe, 2pe + 1)
               const float v0 = v[4 * rq + 2 * pe], v1 = v[4 * rq + 2 * pe + 1];
               const float got = swap_adjacent(odd ? v0 : v1);
-              const unsigned rr = (unsigned)(32 * i + 8 * rq + 2 * pe);
-              buf_st(rd, dofs[j] + rr * ld_s * E, odd ? pack_bf16x2(got, v1) : pack_bf16x2(v0, got));
+              keep[kStageT ? blk : 0][2 * rq + pe] = odd ? pack_bf16x2(got, v1) : pack_bf16x2(v0, got);
             }
           } else {
 #pragma unroll
@@ -1069,6 +1079,33 @@ struct ApplyEpilogue {
         if (sw & 1u) p = u32x4_t{p.z, p.w, p.x, p.y};
         const unsigned o = (unsigned)row0 + 8u * q < ld_t ? (c * ld_t + (unsigned)row0 + 8u * q) * 2u : kOob;
         __builtin_amdgcn_raw_buffer_store_b128(p, rt, (int)o, 0, 0);
+      }
+      // the row-major copy through the same LDS: every lane writes its kept dwords
+      // (two columns of one row) into a row-major 256×256 bf16 tile whose 16-byte
+      // pieces are XOR-swizzled by row_swz, then 16-byte pieces of whole rows go out
+      __syncthreads();
+#pragma unroll
+      for (int blk = 0; blk < 8; ++blk) {
+        const unsigned i = (unsigned)blk >> 1, j = (unsigned)blk & 1;
+        const unsigned cb = ((lc0 + 32u * j) & ~1u) * 2u;           // byte of the column pair in its row
+#pragma unroll
+        for (int rq = 0; rq < 4; ++rq)
+#pragma unroll
+          for (int pe = 0; pe < 2; ++pe) {
+            const unsigned r = lr0 + (odd ? 1u : 0u) + 32u * i + 8u * rq + 2u * pe;
+            *(__attribute__((address_space(3))) uint32_t*)(smem + r * 512u + ((((cb >> 4) ^ row_swz(r)) << 4) | (cb & 15u))) =
+                keep[blk][2 * rq + pe];
+          }
+      }
+      __syncthreads();
+#pragma unroll 4
+      for (int k = 0; k < 16; ++k) {
+        const unsigned id = threadIdx.x + (unsigned)kGemmThreads * k;
+        const unsigned r = id >> 5, q = id & 31;
+        const u32x4_t p = *(const __attribute__((address_space(3))) u32x4_t*)(smem + r * 512u + ((q ^ row_swz(r)) << 4));
+        const unsigned c = (unsigned)col0 + 8u * q;
+        const unsigned o = c < ld_s ? (r * ld_s + c) * 2u : kOob;
+        __builtin_amdgcn_raw_buffer_store_b128(p, rd, (int)o, 0, 0);
       }
     }
   }
