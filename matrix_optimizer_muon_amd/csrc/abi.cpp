@@ -275,35 +275,22 @@ static int run_plan(Plan& pl, char* ws, int prec_f32, const LaunchScalars& base_
 // ---------------------------------------------------------------------------
 constexpr int kMaxGroups = 4;
 
-// Group count from the shape mix and the rounds of apply tiles on the 256 CUs of
-// an MI355X (a fixed count keeps the workspace size a host-only computation).
-// Measured, ms per step with 1 / 2 / 3 / 4 groups:
-// * most apply tiles on slices with a short side <= 1024: one group.  Their
-//   contractions are short and the phases are bound by epilogue traffic, which
-//   concurrency does not relieve (384 matrices of 512 and 256 rows: 3.60 / 3.94 /
-//   4.25 / 4.55);
-// * below 4 rounds: four groups, whose tails and epilogues overlap each other's
-//   mainloops (one d=2048 layer: 3.17 / 2.92 / 2.83 / 2.78);
-// * every slice with the same short side and >= 16 rounds: one group; the tails
-//   are a small share and one sequence keeps the best L2 reuse (Llama d=4096
-//   share: 64.5 / 66.6 / 68.8 / 70.7);
-// * otherwise three (MLP/MoE mix of 8192-wide matrices and 1408-wide experts:
-//   144.9 / 136.7 / 134.5 / 141.6).
+// Group count from the rounds of apply tiles on the 256 CUs of an MI355X (a
+// fixed count keeps the workspace size a host-only computation).  Measured, ms
+// per step with 1 / 2 / 3 / 4 groups:
+// * below 4 rounds: four groups, whose tail rounds and epilogues overlap each
+//   other's contractions (one d=2048 layer: 2.86 / 2.68 / 2.63 / 2.60);
+// * otherwise one: the tails are a small share, and one launch sequence keeps
+//   the operand panels of neighbouring tiles together in each XCD's L2 (Llama
+//   d=4096 share: 60.9 / 63.5; MLP/MoE mix of 8192-wide matrices and 1408-wide
+//   experts: 121.6 / 127.3 / 127.9 / 131.3; 384 small matrices: 3.12 / 3.10–3.72
+//   / 3.47–3.97).
 constexpr int kCusAssumed = 256;
 
 static int group_count(const std::vector<Item>& items) {
-  double tiles = 0, short_tiles = 0;
-  bool same_m = true;
-  const int64_t m0 = std::min(items[0].rows, items[0].cols);
-  for (const Item& it : items) {
-    const int64_t m = std::min(it.rows, it.cols);
-    const double t = (double)it.batch * cdiv(it.rows, kTile) * cdiv(it.cols, kTile);
-    tiles += t;
-    if (m <= 1024) short_tiles += t;
-    same_m = same_m && m == m0;
-  }
-  const double rounds = tiles / kCusAssumed;
-  int g = short_tiles > 0.5 * tiles ? 1 : rounds < 4.0 ? 4 : (same_m && rounds >= 16.0) ? 1 : 3;
+  double tiles = 0;
+  for (const Item& it : items) tiles += (double)it.batch * cdiv(it.rows, kTile) * cdiv(it.cols, kTile);
+  int g = tiles < 4.0 * kCusAssumed ? 4 : 1;
   if (const char* v = std::getenv("DMUON_STREAM_GROUPS")) {   // tuning override, 1..4
     const int x = std::atoi(v);
     if (x >= 1 && x <= kMaxGroups) g = x;
