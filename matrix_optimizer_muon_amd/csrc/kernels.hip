@@ -857,6 +857,7 @@ struct ApplyEpilogue {
   unsigned lr0;
   int row0, col0;
   bool odd, pub_pairs, from0;
+  bool has_w, has_out, has_pub;          // last apply: which outputs exist (workgroup-uniform)
   float xin[kAhead][16];
   float win[LAST ? kAhead : 1][16];
 
@@ -894,6 +895,9 @@ struct ApplyEpilogue {
     // published bf16 copy: two columns per dword when rows hold an even number of
     // columns (a pair never straddles rows), else one 16-bit store per element
     pub_pairs = (P.cols & 1) == 0;
+    has_w = __builtin_amdgcn_readfirstlane(s.write_master ? 1 : 0) != 0;
+    has_out = __builtin_amdgcn_readfirstlane(P.out ? 1 : 0) != 0;
+    has_pub = __builtin_amdgcn_readfirstlane(s.write_master && P.pub ? 1 : 0) != 0;
     if (LAST) {
       const int64_t first = ((int64_t)slice * rows + row0) * P.cols, bytes = (int64_t)trows * P.cols * 4;
       rw = range_rsrc(s.write_master ? P.master + first : nullptr, bytes);
@@ -948,7 +952,7 @@ struct ApplyEpilogue {
         xin[slot][4 * rq + 2] = q.z; xin[slot][4 * rq + 3] = q.w;
       }
     }
-    if (LAST) {
+    if (LAST && has_w) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const unsigned rr = (unsigned)(32 * i + 8 * (r >> 2) + (r & 3));
@@ -995,15 +999,23 @@ struct ApplyEpilogue {
       for (int r = 0; r < 16; ++r) v[r] = xs * fmaf(alpha, xin[slot][r], acc[i][j][r]);
       if (LAST) {
         float w[16];
+        if (has_out) {
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const unsigned rr = (unsigned)(32 * i + 8 * (r >> 2) + (r & 3));
-          const unsigned o = wo[j] + rr * cols * 4u;
-          w[r] = fmaf(-s.lr, v[r], s.decay * win[LAST ? slot : 0][r]);
-          buf_st(ro, o, v[r]);
-          buf_st(rw, o, w[r]);
+          for (int r = 0; r < 16; ++r) {
+            const unsigned rr = (unsigned)(32 * i + 8 * (r >> 2) + (r & 3));
+            buf_st(ro, wo[j] + rr * cols * 4u, v[r]);
+          }
         }
-        if (pub_pairs) {
+        if (has_w) {
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const unsigned rr = (unsigned)(32 * i + 8 * (r >> 2) + (r & 3));
+            w[r] = fmaf(-s.lr, v[r], s.decay * win[LAST ? slot : 0][r]);
+            buf_st(rw, wo[j] + rr * cols * 4u, w[r]);
+          }
+        }
+        if (!has_pub) {
+        } else if (pub_pairs) {
 #pragma unroll
           for (int rq = 0; rq < 4; ++rq)
 #pragma unroll
