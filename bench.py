@@ -415,6 +415,11 @@ def main():
         "roofline": roof,
         "cpu_baseline": cpu,
         "phases_ms_per_step": {k: round(v[0] / args.steps, 4) for k, v in phases.items() if v[1]},
+        # one-stream pass: Newton–Schulz contractions alone, element-wise kernels alone
+        "ns_ms_per_step": round(sum(phases[p][0] for p in ("gram", "square", "apply") if p in phases)
+                                / args.steps, 4) if phases else None,
+        "elementwise_ms_per_step": round(sum(phases[p][0] for p in ("ingest", "norm", "update")
+                                             if p in phases) / args.steps, 4) if phases else None,
         "ms_per_step_one_stream": None if ms_alone is None else round(ms_alone, 4),
         "wall_s_timed": round(wall, 3),
         "device": {"name": props.name, "cus": props.multi_processor_count},
