@@ -199,7 +199,8 @@ static int build_plan(const std::vector<Item>& items, int prec_f32, Plan& pl, ch
     P.pub = it.pub;
     const int64_t b = it.batch;
     const int64_t prep = (int64_t)P.prep_tiles_r * P.prep_tiles_c;
-    P.xf = (float*)carve((size_t)(b * P.apply_tr * P.apply_tc) * kTile * kTile * 4);
+    // the iterate: 24-bit values (3 bytes) on the bf16 path, fp32 on the fp32 path
+    P.xf = (float*)carve((size_t)(b * P.apply_tr * P.apply_tc) * kTile * kTile * (prec_f32 ? 4 : 3));
     if (!it.mom) P.xraw = (float*)carve((size_t)(b * it.rows * P.ld_x) * 4);
     P.xg = carve((size_t)(b * P.m * P.ld_n) * esz);
     P.xa0 = carve((size_t)(b * P.n * P.ld_m) * esz);

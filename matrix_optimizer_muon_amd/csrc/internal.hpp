@@ -57,9 +57,10 @@ struct DevProblem {
   const float* x0;             // X₀ before its 1/(‖B‖_F + eps) scale: the momentum
                                // (ld cols), or for ns_batched xraw (ld ld_x)
   // workspace (operand element type = bf16 or fp32 per precision)
-  float* xf;                   // fp32 iterate in the apply's register order: per 256×256
-                               // tile (row-major tile order) kTile² floats laid out as
-                               // [wave 8][block 8][quad rq 4][lane 64][4 rows]
+  float* xf;                   // iterate in the apply's register order: per 256×256 tile
+                               // (row-major tile order) kTile² values laid out as
+                               // [wave 8][block 8][16-byte piece][lane 64]; 24-bit values
+                               // (3 pieces per block) on the bf16 path, fp32 (4) on the fp32 one
   float* xraw;                 // ns_batched only: x in fp32, storage layout rows×ld_x
   void* xg;                    // oriented X, m×ld_n, stride m*ld_n
   void* xa0;                   // oriented Xᵀ, n×ld_m, stride n*ld_m (ping)

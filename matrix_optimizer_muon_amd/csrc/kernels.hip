@@ -822,9 +822,11 @@ typedef unsigned u32x2_t __attribute__((ext_vector_type(2)));
 //   X' = xs·(α·X + acc), α = a + b·d + c·d²; at t = 0 X is read from the
 //        unscaled source x0 (B, storage layout, 4-byte accesses: each wave
 //        instruction covers two 128-byte row segments) and xs = inv, else xs = 1
-//        and X is the fp32 iterate, which is kept in the order of the registers
-//        (one 16-byte piece per lane and quad rq, 1 KiB contiguous per wave
-//        instruction), so it moves with 4 loads and 4 stores per block
+//        and X is the stored iterate, kept in the order of the registers (16-byte
+//        pieces per lane, 1 KiB contiguous per wave instruction): on the bf16
+//        path 24-bit values (the top 24 bits of the fp32 value, rounded to
+//        nearest even), four per three dwords, so a block moves with 3 loads and
+//        3 stores; on the fp32 path fp32 values, 4 and 4
 //   t < k−1: the row-major operand copy, two columns per dword (even lanes take
 //        rows e = 0, 2 from their odd neighbour, odd lanes rows 1, 3), and the
 //        transposed copy; Σ X'² partial
@@ -850,6 +852,9 @@ struct ApplyEpilogue {
   static constexpr int kAhead = LAST ? 2 : 3;
   static constexpr int kPre = LAST ? 1 : 3;       // blocks loaded before the contraction
   static constexpr unsigned E = sizeof(T);
+  // dwords per 4 values of the stored iterate: 24-bit values on the bf16 path
+  // (whose operands are bf16 anyway), fp32 on the fp32 path
+  static constexpr int kXWords = E == 2 ? 3 : 4;
 
   __amdgpu_buffer_rsrc_t rx, ri, rw, ro, rd, rt, rp;
   unsigned xi[2], wo[2], dofs[2], tofs[2], po[2];
@@ -877,9 +882,9 @@ struct ApplyEpilogue {
     odd = (lane & 1) != 0;
 
     // the iterate's tile: byte (((wave·8 + blk)·4 + rq)·64 + lane)·16
-    rx = range_rsrc(P.xf + ((int64_t)slice * P.apply_tr * P.apply_tc + u) * (kTile * kTile),
-                    (int64_t)kTile * kTile * 4);
-    xb = (unsigned)((wave * 8 * 4 * 64 + lane) * 16);
+    rx = range_rsrc(P.xf + ((int64_t)slice * P.apply_tr * P.apply_tc + u) * (kTile * kTile / 4 * kXWords),
+                    (int64_t)kTile * kTile * kXWords);
+    xb = (unsigned)((wave * 8 * kXWords * 64 + lane) * 16);
     // the X₀ read at t = 0: the unscaled source in storage layout
     from0 = s.t == 0;
     ldi = (unsigned)P.ld_x0;
@@ -931,9 +936,37 @@ struct ApplyEpilogue {
     }
   }
 
-  // byte offset of quad rq of block blk in the iterate's tile
-  __device__ __forceinline__ unsigned xq(int blk, int rq) const {
-    return xb + (unsigned)((blk * 4 + rq) * 64 * 16);
+  // byte offset of 16-byte piece q of block blk in the iterate's tile
+  __device__ __forceinline__ unsigned xq(int blk, int q) const {
+    return xb + (unsigned)((blk * kXWords + q) * 64 * 16);
+  }
+
+  // 24-bit iterate (bf16 path): the top 24 bits of the fp32 value, rounded to
+  // nearest even; four values go into three dwords
+  static __device__ __forceinline__ uint32_t enc24(float f) {
+    const uint32_t u = __float_as_uint(f);
+    return (u + 0x7Fu + ((u >> 8) & 1u)) >> 8;
+  }
+  static __device__ __forceinline__ void pack24(const float (&v)[16], uint32_t (&w)[12]) {
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      const uint32_t c0 = enc24(v[4 * g]), c1 = enc24(v[4 * g + 1]), c2 = enc24(v[4 * g + 2]),
+                     c3 = enc24(v[4 * g + 3]);
+      w[3 * g] = c0 | (c1 << 24);
+      w[3 * g + 1] = (c1 >> 8) | (c2 << 16);
+      w[3 * g + 2] = (c2 >> 16) | (c3 << 8);
+    }
+  }
+  static __device__ __forceinline__ void unpack24(const float (&in)[16], float (&x)[16]) {
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      const uint32_t d0 = __float_as_uint(in[3 * g]), d1 = __float_as_uint(in[3 * g + 1]),
+                     d2 = __float_as_uint(in[3 * g + 2]);
+      x[4 * g] = __uint_as_float((d0 & 0xFFFFFFu) << 8);
+      x[4 * g + 1] = __uint_as_float(((d0 >> 24) | ((d1 & 0xFFFFu) << 8)) << 8);
+      x[4 * g + 2] = __uint_as_float(((d1 >> 16) | ((d2 & 0xFFu) << 16)) << 8);
+      x[4 * g + 3] = __uint_as_float(d2 & 0xFFFFFF00u);
+    }
   }
 
   __device__ __forceinline__ void load_blk(int blk, int slot) {
@@ -946,10 +979,10 @@ struct ApplyEpilogue {
       }
     } else {
 #pragma unroll
-      for (int rq = 0; rq < 4; ++rq) {
-        const f32x4_t q = __builtin_amdgcn_raw_buffer_load_b128(rx, (int)xq(blk, rq), 0, 0);
-        xin[slot][4 * rq] = q.x; xin[slot][4 * rq + 1] = q.y;
-        xin[slot][4 * rq + 2] = q.z; xin[slot][4 * rq + 3] = q.w;
+      for (int q = 0; q < kXWords; ++q) {
+        const f32x4_t w = __builtin_amdgcn_raw_buffer_load_b128(rx, (int)xq(blk, q), 0, 0);
+        xin[slot][4 * q] = w.x; xin[slot][4 * q + 1] = w.y;
+        xin[slot][4 * q + 2] = w.z; xin[slot][4 * q + 3] = w.w;
       }
     }
     if (LAST && has_w) {
@@ -995,8 +1028,14 @@ struct ApplyEpilogue {
       const int slot = blk % kAhead;
       const int i = blk >> 1, j = blk & 1;
       float v[16];
+      if (kXWords == 3 && !from0) {
+        unpack24(xin[slot], v);
+      } else {
 #pragma unroll
-      for (int r = 0; r < 16; ++r) v[r] = xs * fmaf(alpha, xin[slot][r], acc[i][j][r]);
+        for (int r = 0; r < 16; ++r) v[r] = xin[slot][r];
+      }
+#pragma unroll
+      for (int r = 0; r < 16; ++r) v[r] = xs * fmaf(alpha, v[r], acc[i][j][r]);
       if (LAST) {
         float w[16];
         if (has_out) {
@@ -1035,10 +1074,19 @@ struct ApplyEpilogue {
       } else {
 #pragma unroll
         for (int r = 0; r < 16; ++r) sq = fmaf(v[r], v[r], sq);
+        if constexpr (kXWords == 3) {
+          uint32_t w[12];
+          pack24(v, w);
 #pragma unroll
-        for (int rq = 0; rq < 4; ++rq)
-          __builtin_amdgcn_raw_buffer_store_b128(
-              f32x4_t{v[4 * rq], v[4 * rq + 1], v[4 * rq + 2], v[4 * rq + 3]}, rx, (int)xq(blk, rq), 0, 0);
+          for (int q = 0; q < 3; ++q)
+            __builtin_amdgcn_raw_buffer_store_b128(u32x4_t{w[4 * q], w[4 * q + 1], w[4 * q + 2], w[4 * q + 3]}, rx,
+                                                   (int)xq(blk, q), 0, 0);
+        } else {
+#pragma unroll
+          for (int rq = 0; rq < 4; ++rq)
+            __builtin_amdgcn_raw_buffer_store_b128(
+                f32x4_t{v[4 * rq], v[4 * rq + 1], v[4 * rq + 2], v[4 * rq + 3]}, rx, (int)xq(blk, rq), 0, 0);
+        }
         // transposed copy: four consecutive rows of one column
 #pragma unroll
         for (int rq = 0; rq < 4; ++rq) {
