@@ -202,9 +202,15 @@ static int build_plan(const std::vector<Item>& items, int prec_f32, Plan& pl, ch
     // the iterate: 24-bit values (3 bytes) on the bf16 path, fp32 on the fp32 path
     P.xf = (float*)carve((size_t)(b * P.apply_tr * P.apply_tc) * kTile * kTile * (prec_f32 ? 4 : 3));
     if (!it.mom) P.xraw = (float*)carve((size_t)(b * it.rows * P.ld_x) * 4);
-    P.xg = carve((size_t)(b * P.m * P.ld_n) * esz);
-    P.xa0 = carve((size_t)(b * P.n * P.ld_m) * esz);
-    P.xa1 = carve((size_t)(b * P.n * P.ld_m) * esz);
+    if (prec_f32) {
+      P.xg = carve((size_t)(b * P.m * P.ld_n) * esz);
+      P.xa0 = carve((size_t)(b * P.n * P.ld_m) * esz);
+      P.xa1 = carve((size_t)(b * P.n * P.ld_m) * esz);
+    } else {
+      const int64_t ld_s = round_up(it.cols, kLdAlign);
+      P.xs[0] = carve((size_t)(b * it.rows * ld_s) * esz);
+      P.xs[1] = carve((size_t)(b * it.rows * ld_s) * esz);
+    }
     P.ap = carve((size_t)(b * P.m * P.ld_m) * esz);
     P.bp = carve((size_t)(b * P.m * P.ld_m) * esz);
     P.part_norm = (float*)carve((size_t)(b * prep) * 4);

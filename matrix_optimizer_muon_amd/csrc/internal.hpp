@@ -62,6 +62,11 @@ struct DevProblem {
                                // [wave 8][block 8][16-byte piece][lane 64]; 24-bit values
                                // (3 pieces per block) on the bf16 path, fp32 (4) on the fp32 one
   float* xraw;                 // ns_batched only: x in fp32, storage layout rows×ld_x
+  void* xs[2];                 // bf16 path: X in storage layout, rows×ld_s with
+                               // ld_s = round_up(cols, 64) (ping-pong: the apply reads
+                               // xs[t & 1] and writes xs[(t + 1) & 1]); every bf16
+                               // contraction reads X from it, row-major or K-major
+  // fp32 path (no K-major reads there): both orientations of X
   void* xg;                    // oriented X, m×ld_n, stride m*ld_n
   void* xa0;                   // oriented Xᵀ, n×ld_m, stride n*ld_m (ping)
   void* xa1;                   // (pong)

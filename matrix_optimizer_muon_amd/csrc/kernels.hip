@@ -36,6 +36,7 @@ typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 typedef unsigned u32x4_t __attribute__((ext_vector_type(4)));
+typedef short v4i16_t __attribute__((ext_vector_type(4)));
 
 // Global-memory (address space 1) view of a pointer.  Pointers read out of the
 // device-side problem table are generic to the compiler, which would otherwise
@@ -170,9 +171,9 @@ __global__ __launch_bounds__(kThreads) void k_norm(LaunchTable tab, LaunchScalar
 // ---------------------------------------------------------------------------
 // ingest: one 64×64 storage tile of one slice per workgroup
 //   B ← μB + s·G into the momentum (for NS alone X = x, kept in fp32 in the
-//   iterate buffer), the tile's partial Σ B², and the operand copies of B in
-//   storage layout and transposed (through an LDS tile), unscaled, with zero
-//   padding up to the 64-element leading dims.
+//   iterate buffer), the tile's partial Σ B², and the unscaled operand copy of B
+//   in storage layout, with zero padding up to the 64-element leading dim (the
+//   fp32 path also writes the transposed copy, through an LDS tile).
 // The scale of X₀ = inv·B, inv = 1/(‖B‖_F + eps), is applied by the first Gram
 // (A'₀ = inv²·B Bᵀ − d₀·I) and the first apply (X₁ = inv·(α·B + B'₀·B)), which
 // is the same algebra, so B is read once and no scaled copy of it is written.
@@ -198,8 +199,11 @@ __global__ __launch_bounds__(kThreads) void k_ingest(LaunchTable tab, LaunchScal
   float* xf = s.has_momentum ? nullptr : P.xraw + (int64_t)slice * rows * P.ld_x;
   const int ld_s = P.wide ? P.ld_n : P.ld_m;    // straight copy: cols padded
   const int ld_t = P.wide ? P.ld_m : P.ld_n;    // transposed copy: rows padded
-  T* cs = (T*)(P.wide ? P.xg : P.xa0) + (int64_t)slice * rows * ld_s;
-  T* ct = (T*)(P.wide ? P.xa0 : P.xg) + (int64_t)slice * cols * ld_t;
+  // bf16: the storage-layout copy only (every bf16 contraction reads X from it);
+  // fp32: the storage-layout copy and the transposed one
+  constexpr bool kBoth = sizeof(T) == 4;
+  T* cs = (T*)(kBoth ? (P.wide ? P.xg : P.xa0) : P.xs[0]) + (int64_t)slice * rows * ld_s;
+  T* ct = kBoth ? (T*)(P.wide ? P.xa0 : P.xg) + (int64_t)slice * cols * ld_t : nullptr;
   // rows of 4-element vectors are aligned when cols is a multiple of 4 and the
   // slice bases are (16 bytes for fp32 data, 8 for bf16)
   const bool vec = (cols & 3) == 0 &&
@@ -258,14 +262,17 @@ __global__ __launch_bounds__(kThreads) void k_ingest(LaunchTable tab, LaunchScal
       if (xf && c < cols) *(float4*)(xf + (int64_t)r * P.ld_x + c) = make_float4(v[0], v[1], v[2], v[3]);
       if (c < ld_s) store4(cs + (int64_t)r * ld_s + c, v[0], v[1], v[2], v[3]);
     }
+    if (kBoth) {
 #pragma unroll
-    for (int e = 0; e < 4; ++e) tile[lr][tc + e] = v[e];
+      for (int e = 0; e < 4; ++e) tile[lr][tc + e] = v[e];
+    }
   }
   // (3) the tile's Σ B² (its barriers also publish the LDS tile)
   const float tot = block_sum<4>(sq, red);
   if (threadIdx.x == 0) P.part_norm[(int64_t)slice * per_slice + tt] = tot;
-  // (4) transposed copy: 64 storage columns × 64 storage rows = 8 chunks of 8
-  // rows (bf16) or 16 chunks of 4 rows (fp32) per column
+  if (!kBoth) return;
+  // (4) fp32: transposed copy: 64 storage columns × 64 storage rows = 16 chunks
+  // of 4 rows per column
   constexpr int RPC = 16 / (int)sizeof(T);
   constexpr int CPC = kPrepTile / RPC;
 #pragma unroll
@@ -423,8 +430,32 @@ __global__ __launch_bounds__(kThreads) void k_adamw(AdamwTable tab, AdamwScalars
   }
 }
 
+// Buffer resource over [p, p + bytes) (a null p gives an empty range).  Buffer
+// accesses are range checked: a load beyond the range reads zero and a store
+// beyond it is dropped, which replaces per-element predicates (and the branches
+// they would need) in the apply epilogue.
+constexpr unsigned kOob = 0x7ffffff0u;       // an offset beyond every range used here
+// The fields are workgroup-uniform; readfirstlane tells the compiler so (a
+// descriptor it cannot prove uniform is rebuilt per lane in a loop).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t range_rsrc(const void* p, int64_t bytes) {
+  const uint64_t a = (uint64_t)(uintptr_t)p;
+  const unsigned lo = __builtin_amdgcn_readfirstlane((unsigned)a);
+  const unsigned hi = __builtin_amdgcn_readfirstlane((unsigned)(a >> 32));
+  const int n = __builtin_amdgcn_readfirstlane(p ? (int)bytes : 0);
+  return __builtin_amdgcn_make_buffer_rsrc((void*)(((uint64_t)hi << 32) | lo), 0, n, 0x00020000);
+}
+__device__ __forceinline__ float buf_ld(__amdgpu_buffer_rsrc_t r, unsigned off) {
+  return __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(r, (int)off, 0, 0));
+}
+__device__ __forceinline__ void buf_st(__amdgpu_buffer_rsrc_t r, unsigned off, float v) {
+  __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v), r, (int)off, 0, 0);
+}
+__device__ __forceinline__ void buf_st(__amdgpu_buffer_rsrc_t r, unsigned off, uint32_t v) {
+  __builtin_amdgcn_raw_buffer_store_b32(v, r, (int)off, 0, 0);
+}
+
 // ---------------------------------------------------------------------------
-// NT contraction core on the matrix cores.
+// Contraction core on the matrix cores: C[i][j] = Σ_k A(i, k)·B(j, k).
 //
 // One workgroup = 8 wave64s (two per SIMD) computing a 256×256 output tile; each
 // wave owns a 128×64 sub-tile (4×2 blocks of 32×32 MFMA output).  K is staged
@@ -433,6 +464,18 @@ __global__ __launch_bounds__(kThreads) void k_adamw(AdamwTable tab, AdamwScalars
 // operand read as zero through the buffer's range check).  The four 16-byte
 // chunks of a row are XOR-swizzled with (row >> 2) & 3 so that 16 consecutive
 // rows read at one logical chunk cover all 64 LDS banks.
+//
+// An operand is read either row-major ("NT": row i holds A(i, 0..K), staged as
+// 256 rows of 64 bytes) or K-major (row k holds A(0..255, k) of the tile,
+// staged as 32 rows of 512 bytes, bf16 only).  A K-major stage is filled with
+// whole 512-byte row segments, so each DMA instruction moves 8 full cache lines
+// (the NT stage moves 16 half lines); its MFMA fragments are read with the
+// transposing ds_read_b64_tr_b16 (two 8-byte reads per 16-byte fragment).  Its
+// 32-byte segments are XOR-swizzled by 2·(row & 3), which spreads the 8 rows × 2
+// segments one fragment read touches over all 64 banks.  K-major reads of a
+// bf16 operand were 5–16% faster than NT ones for the B operand of 2048- to
+// 8192-sized products, which is why symmetric operands (A′, B′) and the stored
+// X are read K-major wherever the product allows it.
 //
 // Ping-pong schedule: the two waves sharing a SIMD belong to different groups
 // (group = wave >> 2, the 128-row half of the tile they own), and the groups run
@@ -452,14 +495,19 @@ constexpr int kDmaPerStage = 4;                        // buffer_load … lds pe
 static_assert(kTile == 256 && kGemmWaves == 8, "fragment layout assumes 8 waves on a 256 tile");
 
 struct Operands {
-  const char* a;     // first A row of the tile
-  const char* b;     // first B row of the tile
+  const char* a;     // NT: first A row of the tile; K-major: start of k-row 0
+  const char* b;     // NT: first B row of the tile; K-major: start of k-row 0
   int lda_b;         // leading dims in bytes (multiples of 128)
   int ldb_b;
-  int rows_a;        // valid rows from the tile start
+  int rows_a;        // NT: valid rows from the tile start; K-major: valid k rows
   int rows_b;
-  int ktiles;        // K bytes per row / 64
+  int cola_b;        // K-major: byte offset of the tile's first column in a k-row
+  int colb_b;
+  int ktiles;        // stages: K elements / 32 (bf16) or / 16 (fp32)
 };
+
+// K-major stage layout: 32-byte segment s of k-row r sits at segment s ^ kmaj_swz(r)
+__device__ __forceinline__ int kmaj_swz(int r) { return 2 * (r & 3); }
 
 template <typename T>
 __device__ __forceinline__ void mfma_chunk(f32x16_t& acc, const u32x4_t& a, const u32x4_t& b);
@@ -489,8 +537,9 @@ __device__ __forceinline__ void mfma_chunk<float>(f32x16_t& acc, const u32x4_t& 
 // s_waitcnt with only lgkmcnt constrained to 0 (vmcnt 63, expcnt 7 = no wait)
 #define DMUON_WAIT_LGKM0() __builtin_amdgcn_s_waitcnt(0xF | (0x3 << 14) | (0x7 << 4))
 
-template <typename T>
+template <typename T, bool TA = false, bool TB = false>
 __device__ __forceinline__ void gemm_mainloop(const Operands& op, char* smem, f32x16_t (&acc)[4][2]) {
+  static_assert(!(TA || TB) || sizeof(T) == 2, "K-major operands are bf16");
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);    // wave-uniform
   const int wr = wave >> 2, wc = wave & 3, h = lane >> 5, r32 = lane & 31;
@@ -500,13 +549,17 @@ __device__ __forceinline__ void gemm_mainloop(const Operands& op, char* smem, f3
       (void*)op.b, 0, (op.rows_b < kTile ? op.rows_b : kTile) * op.ldb_b, 0x00020000);
   // DMA: wave w fills rows [32w, 32w + 32) of A and of B, 16 rows per instruction;
   // lane l lands at byte 16·l of the instruction's 1 KiB = row l/4, physical chunk l%4.
+  // K-major: the instruction's 1 KiB is k-rows 2(2w + q) and 2(2w + q) + 1; lane l
+  // lands in k-row l/32 at physical 16-byte unit l%32.
   int offa[2], offb[2];
 #pragma unroll
   for (int q = 0; q < 2; ++q) {
     const int row = (wave * 2 + q) * 16 + (lane >> 2);
     const int c = (lane & 3) ^ ((row >> 2) & 3);
-    offa[q] = row * op.lda_b + c * 16;
-    offb[q] = row * op.ldb_b + c * 16;
+    const int kr = 2 * (wave * 2 + q) + (lane >> 5), un = lane & 31;
+    const int lun = (((un >> 1) ^ kmaj_swz(kr)) << 1) | (un & 1);    // logical unit
+    offa[q] = TA ? kr * op.lda_b + op.cola_b + lun * 16 : row * op.lda_b + c * 16;
+    offb[q] = TB ? kr * op.ldb_b + op.colb_b + lun * 16 : row * op.ldb_b + c * 16;
   }
   // fragment offsets inside a stage for logical chunk 2·ss + h
   int fa_off[2][4], fb_off[2][2];
@@ -524,6 +577,32 @@ __device__ __forceinline__ void gemm_mainloop(const Operands& op, char* smem, f3
       fb_off[ss][j] = kTile * kRowBytes + row * kRowBytes + ((c ^ ((row >> 2) & 3)) * 16);
     }
   }
+  // K-major fragments: two transposing 8-byte reads (k 0..3 and 4..7 of the
+  // lane's 8-k block); in each 16-lane group, source lane i reads k-row i >> 2,
+  // columns 4(i & 3) .. +3 of the group's 16 columns, and lane i receives column
+  // i of the group, four consecutive k
+  int ta_off[TA ? 2 : 1][4][2], tb_off[TB ? 2 : 1][2][2];
+#pragma unroll
+  for (int ss = 0; ss < 2; ++ss)
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+      const int kr = 16 * ss + 8 * h + 4 * t + ((lane & 15) >> 2);
+      const int sub = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
+      if (TA) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int n = wr * 128 + i * 32 + sub;
+          ta_off[TA ? ss : 0][i][t] = kr * 512 + (((n >> 4) ^ kmaj_swz(kr)) << 5) + ((2 * n) & 31);
+        }
+      }
+      if (TB) {
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+          const int n = wc * 64 + j * 32 + sub;
+          tb_off[TB ? ss : 0][j][t] = kTile * kRowBytes + kr * 512 + (((n >> 4) ^ kmaj_swz(kr)) << 5) + ((2 * n) & 31);
+        }
+      }
+    }
 #pragma unroll
   for (int i = 0; i < 4; ++i)
 #pragma unroll
@@ -532,16 +611,27 @@ __device__ __forceinline__ void gemm_mainloop(const Operands& op, char* smem, f3
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
 
   u32x4_t fa[2][4], fb[2][2];     // all fragments of one stage
+  // K-major operands take a range per stage: exactly its 32 k-rows (fewer at the
+  // K tail, whose missing rows read as zero), so byte offsets stay small for any
+  // K and no read leaves the operand.  Reads past a row's end (tile columns past
+  // the leading dim) see the next row or zero; they feed only output columns
+  // past the matrix, which the epilogues drop.
+  auto kmaj_rsrc = [&](const char* p, int ld_b, int rows, int kt) {
+    const int left = rows - 32 * kt;
+    return range_rsrc(p + (int64_t)kt * 32 * ld_b, (int64_t)(left < 0 ? 0 : (left < 32 ? left : 32)) * ld_b);
+  };
   auto issue = [&](int kt) {
     char* base = smem + (kt % kStages) * kStageBytes;
+    const __amdgpu_buffer_rsrc_t sa = TA ? kmaj_rsrc(op.a, op.lda_b, op.rows_a, kt) : ra;
+    const __amdgpu_buffer_rsrc_t sb = TB ? kmaj_rsrc(op.b, op.ldb_b, op.rows_b, kt) : rb;
 #pragma unroll
     for (int q = 0; q < 2; ++q) {
       char* da = base + (wave * 2 + q) * 16 * kRowBytes;
       char* db = da + kTile * kRowBytes;
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (__attribute__((address_space(3))) void*)da, 16,
-                                               offa[q] + kt * kRowBytes, 0, 0, 0);
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, (__attribute__((address_space(3))) void*)db, 16,
-                                               offb[q] + kt * kRowBytes, 0, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(sa, (__attribute__((address_space(3))) void*)da, 16,
+                                               offa[q] + (TA ? 0 : kt * kRowBytes), 0, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(sb, (__attribute__((address_space(3))) void*)db, 16,
+                                               offb[q] + (TB ? 0 : kt * kRowBytes), 0, 0, 0);
     }
   };
   const int KT = op.ktiles;        // ≥ 2 (leading dims are multiples of 64 elements)
@@ -556,12 +646,26 @@ __device__ __forceinline__ void gemm_mainloop(const Operands& op, char* smem, f3
     if (kt + 2 < KT) DMUON_WAIT_VM(kDmaPerStage);
     else DMUON_WAIT_VM(0);
     const char* base = smem + (kt % kStages) * kStageBytes;
+    auto tr16 = [&](int off0, int off1) {    // two transposing reads → one 16-byte fragment
+      const v4i16_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4i16_t*)(base + off0));
+      const v4i16_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4i16_t*)(base + off1));
+      u32x4_t r;
+      r.x = (uint32_t)(uint16_t)lo.x | ((uint32_t)(uint16_t)lo.y << 16);
+      r.y = (uint32_t)(uint16_t)lo.z | ((uint32_t)(uint16_t)lo.w << 16);
+      r.z = (uint32_t)(uint16_t)hi.x | ((uint32_t)(uint16_t)hi.y << 16);
+      r.w = (uint32_t)(uint16_t)hi.z | ((uint32_t)(uint16_t)hi.w << 16);
+      return r;
+    };
 #pragma unroll
     for (int ss = 0; ss < 2; ++ss) {
 #pragma unroll
-      for (int i = 0; i < 4; ++i) fa[ss][i] = *(const u32x4_t*)(base + fa_off[ss][i]);
+      for (int i = 0; i < 4; ++i)
+        fa[ss][i] = TA ? tr16(ta_off[TA ? ss : 0][i][0], ta_off[TA ? ss : 0][i][1])
+                       : *(const u32x4_t*)(base + fa_off[ss][i]);
 #pragma unroll
-      for (int j = 0; j < 2; ++j) fb[ss][j] = *(const u32x4_t*)(base + fb_off[ss][j]);
+      for (int j = 0; j < 2; ++j)
+        fb[ss][j] = TB ? tr16(tb_off[TB ? ss : 0][j][0], tb_off[TB ? ss : 0][j][1])
+                       : *(const u32x4_t*)(base + fb_off[ss][j]);
     }
     // the slot of stage kt − 1, read by both groups in earlier phases
     if (kt + kStages - 1 < KT) issue(kt + kStages - 1);
@@ -790,29 +894,6 @@ __device__ __forceinline__ float swap_adjacent(float x) {
   return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0xB1, 0xF, 0xF, false));
 }
 
-// Buffer resource over [p, p + bytes) (a null p gives an empty range).  Buffer
-// accesses are range checked: a load beyond the range reads zero and a store
-// beyond it is dropped, which replaces per-element predicates (and the branches
-// they would need) in the apply epilogue.
-constexpr unsigned kOob = 0x7ffffff0u;       // an offset beyond every range used here
-// The fields are workgroup-uniform; readfirstlane tells the compiler so (a
-// descriptor it cannot prove uniform is rebuilt per lane in a loop).
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t range_rsrc(const void* p, int64_t bytes) {
-  const uint64_t a = (uint64_t)(uintptr_t)p;
-  const unsigned lo = __builtin_amdgcn_readfirstlane((unsigned)a);
-  const unsigned hi = __builtin_amdgcn_readfirstlane((unsigned)(a >> 32));
-  const int n = __builtin_amdgcn_readfirstlane(p ? (int)bytes : 0);
-  return __builtin_amdgcn_make_buffer_rsrc((void*)(((uint64_t)hi << 32) | lo), 0, n, 0x00020000);
-}
-__device__ __forceinline__ float buf_ld(__amdgpu_buffer_rsrc_t r, unsigned off) {
-  return __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(r, (int)off, 0, 0));
-}
-__device__ __forceinline__ void buf_st(__amdgpu_buffer_rsrc_t r, unsigned off, float v) {
-  __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v), r, (int)off, 0, 0);
-}
-__device__ __forceinline__ void buf_st(__amdgpu_buffer_rsrc_t r, unsigned off, uint32_t v) {
-  __builtin_amdgcn_raw_buffer_store_b32(v, r, (int)off, 0, 0);
-}
 typedef unsigned u32x2_t __attribute__((ext_vector_type(2)));
 
 // ---- apply epilogue, in the accumulator layout (no LDS, no barrier, no branch).
@@ -831,22 +912,13 @@ typedef unsigned u32x2_t __attribute__((ext_vector_type(2)));
 //        rows e = 0, 2 from their odd neighbour, odd lanes rows 1, 3), and the
 //        transposed copy; Σ X'² partial
 //   last:  W ← (1 − lr·wd)·W − lr·X', optional copy of X' to the output.
-// The bf16 transposed copy is staged in LDS (free once the contraction is done):
-// each lane writes the four consecutive rows it holds of one column as 8 bytes
-// into a 256×256 bf16 tile stored transposed, 8-byte units XOR-swizzled by the
-// column so that 32 lanes writing 32 columns hit distinct banks; after a barrier
-// every thread stores 16-byte pieces of whole transposed rows (512 contiguous
-// bytes per 32 lanes).  Stored directly, each lane would write 8 scattered bytes.
-// The fp32 copy (fp32 path) does not fit in LDS and is stored directly, four
-// rows per 16-byte store.
-// The X (and W) loads run ahead of the arithmetic by three blocks (two on the
-// last apply).  The first kPre blocks are loaded before the contraction starts
-// (prefetch), so their latency hides behind it instead of stalling every
-// workgroup at once when the tiles of a round finish together.  All ranges start
-// at the tile's first row (byte offsets then fit in 32 bits); rows past the
-// matrix fall outside them, columns past it get the kOob offset.  Out-of-range
-// rows and columns hold zero in acc (zero-filled operands) and read X as zero,
-// so the zero padding of the operand copies is rewritten with zeros.
+// The bf16 copy of X' goes out through LDS (free once the contraction is done):
+// during the block loop each lane packs two columns of one row per dword (lane
+// exchange with its neighbour) and keeps the dwords; after the Σ X'² reduction
+// they are written into a row-swizzled 256×256 bf16 tile and stored as 16-byte
+// pieces of whole rows.  The bf16 path keeps only this storage-layout copy: every
+// bf16 contraction reads it row-major or K-major.  The fp32 path (no K-major
+// reads) stores the row-major and the transposed copy directly.
 template <typename T, bool LAST>
 struct ApplyEpilogue {
   static constexpr int kAhead = LAST ? 2 : 3;
@@ -862,6 +934,7 @@ struct ApplyEpilogue {
   unsigned lr0;
   int row0, col0;
   bool odd, pub_pairs, from0;
+  bool colok[2];                         // the lane's column of block j lies inside the matrix
   bool has_w, has_out, has_pub;          // last apply: which outputs exist (workgroup-uniform)
   float xin[kAhead][16];
   float win[LAST ? kAhead : 1][16];
@@ -880,6 +953,8 @@ struct ApplyEpilogue {
     lr0 = (unsigned)(wr * 128 + h * 4);                 // tile row of register e = 0 (i = rq = 0)
     const int lc0 = wc * 64 + r32;                      // tile column of block j = 0
     odd = (lane & 1) != 0;
+#pragma unroll
+    for (int j = 0; j < 2; ++j) colok[j] = lc0 + 32 * j < tcols;
 
     // the iterate's tile: byte (((wave·8 + blk)·4 + rq)·64 + lane)·16
     rx = range_rsrc(P.xf + ((int64_t)slice * P.apply_tr * P.apply_tc + u) * (kTile * kTile / 4 * kXWords),
@@ -919,11 +994,15 @@ struct ApplyEpilogue {
     } else {
       ld_s = (unsigned)(P.wide ? P.ld_n : P.ld_m);
       ld_t = (unsigned)(P.wide ? P.ld_m : P.ld_n);
+      // bf16: the next storage-layout copy; fp32: the row-major and transposed copies
       void* xa_next = (s.t & 1) ? P.xa0 : P.xa1;
-      const T* dst = (const T*)(P.wide ? P.xg : xa_next) + (int64_t)slice * rows * ld_s;
-      const T* dstT = (const T*)(P.wide ? xa_next : P.xg) + (int64_t)slice * P.cols * ld_t;
+      const T* dst = (const T*)(E == 2 ? P.xs[(s.t + 1) & 1] : (P.wide ? P.xg : xa_next)) +
+                     (int64_t)slice * rows * ld_s;
       rd = range_rsrc(dst + (int64_t)row0 * ld_s, (int64_t)trows * ld_s * E);
-      rt = range_rsrc(dstT + (int64_t)col0 * ld_t, (int64_t)tcols * ld_t * E);
+      if (E != 2) {
+        const T* dstT = (const T*)(P.wide ? xa_next : P.xg) + (int64_t)slice * P.cols * ld_t;
+        rt = range_rsrc(dstT + (int64_t)col0 * ld_t, (int64_t)tcols * ld_t * E);
+      }
 #pragma unroll
       for (int j = 0; j < 2; ++j) {
         // row-major copy: the lane's dword starts at an even column
@@ -1006,18 +1085,12 @@ struct ApplyEpilogue {
     return ((r & 1u) | ((r >> 1) & 2u)) << 2;
   }
 
-  // byte offset in the LDS-staged transposed tile of the 8-byte unit that holds
-  // tile rows 4·unit .. 4·unit + 3 of tile column c
-  static __device__ __forceinline__ unsigned t_stage_off(unsigned c, unsigned unit) {
-    return c * 512u + ((unit ^ (c & 31u)) << 3);
-  }
-
   __device__ __forceinline__ void finish(const DevProblem& P, const LaunchScalars& s, f32x16_t (&acc)[4][2],
                                          int slice, int u, float d, float xs, char* smem, float* red) {
-    constexpr bool kStageT = E == 2 && !LAST;
-    // bf16 row-major copy, staged after the transposed one: the dword each lane
-    // would store per block and (quad rq, pair pe), kept until LDS is free again
-    uint32_t keep[kStageT ? 8 : 1][8];
+    constexpr bool kStage = E == 2 && !LAST;
+    // bf16 copy (storage layout), staged through LDS after the block loop: the
+    // dword each lane would store per block and (quad rq, pair pe)
+    uint32_t keep[kStage ? 8 : 1][8];
     const unsigned lc0 = (unsigned)(((threadIdx.x >> 6) & 3) * 64 + (threadIdx.x & 31));
     const float alpha = s.a + s.b * d + s.c * d * d;
     float sq = 0.f;
@@ -1034,8 +1107,10 @@ struct ApplyEpilogue {
 #pragma unroll
         for (int r = 0; r < 16; ++r) v[r] = xin[slot][r];
       }
+      // columns past the matrix are zero: a K-major operand can feed them values
+      // read past a row's end, which must not reach Σ X'² or any store
 #pragma unroll
-      for (int r = 0; r < 16; ++r) v[r] = xs * fmaf(alpha, v[r], acc[i][j][r]);
+      for (int r = 0; r < 16; ++r) v[r] = colok[j] ? xs * fmaf(alpha, v[r], acc[i][j][r]) : 0.f;
       if (LAST) {
         float w[16];
         if (has_out) {
@@ -1087,14 +1162,11 @@ struct ApplyEpilogue {
             __builtin_amdgcn_raw_buffer_store_b128(
                 f32x4_t{v[4 * rq], v[4 * rq + 1], v[4 * rq + 2], v[4 * rq + 3]}, rx, (int)xq(blk, rq), 0, 0);
         }
-        // transposed copy: four consecutive rows of one column
+        // fp32 path: the transposed copy, four consecutive rows of one column
+        if constexpr (E != 2) {
 #pragma unroll
-        for (int rq = 0; rq < 4; ++rq) {
-          const unsigned rr = (unsigned)(32 * i + 8 * rq);
-          if constexpr (kStageT) {
-            const u32x2_t w2 = {pack_bf16x2(v[4 * rq], v[4 * rq + 1]), pack_bf16x2(v[4 * rq + 2], v[4 * rq + 3])};
-            *(__attribute__((address_space(3))) u32x2_t*)(smem + t_stage_off(lc0 + 32u * j, (lr0 + rr) >> 2)) = w2;
-          } else {
+          for (int rq = 0; rq < 4; ++rq) {
+            const unsigned rr = (unsigned)(32 * i + 8 * rq);
             const unsigned o = (unsigned)row0 + lr0 + rr < ld_t ? tofs[j] + rr * E : kOob;
             const u32x4_t w4 = {__float_as_uint(v[4 * rq]), __float_as_uint(v[4 * rq + 1]),
                                 __float_as_uint(v[4 * rq + 2]), __float_as_uint(v[4 * rq + 3])};
@@ -1109,7 +1181,7 @@ struct ApplyEpilogue {
             for (int pe = 0; pe < 2; ++pe) {        // register pair (2pe, 2pe + 1)
               const float v0 = v[4 * rq + 2 * pe], v1 = v[4 * rq + 2 * pe + 1];
               const float got = swap_adjacent(odd ? v0 : v1);
-              keep[kStageT ? blk : 0][2 * rq + pe] = odd ? pack_bf16x2(got, v1) : pack_bf16x2(v0, got);
+              keep[kStage ? blk : 0][2 * rq + pe] = odd ? pack_bf16x2(got, v1) : pack_bf16x2(v0, got);
             }
           } else {
 #pragma unroll
@@ -1123,27 +1195,14 @@ struct ApplyEpilogue {
       if (blk + kAhead < 8) load_blk(blk + kAhead, slot);
     }
     if (!LAST) {
-      // (the barriers of the sum also publish the staged transposed tile)
       const float tot = block_sum<kGemmWaves>(sq, red);
       if (threadIdx.x == 0) P.part_apply[(int64_t)slice * P.apply_tr * P.apply_tc + u] = tot;
     }
-    if constexpr (kStageT) {
-      // 256 transposed rows × 32 pieces of 16 bytes (tile rows 8q .. 8q + 7)
-#pragma unroll 4
-      for (int k = 0; k < 16; ++k) {
-        const unsigned id = threadIdx.x + (unsigned)kGemmThreads * k;
-        const unsigned c = id >> 5, q = id & 31;
-        const unsigned sw = c & 31u;
-        // logical units 2q, 2q + 1 sit at 2(q ^ sw/2) + (sw & 1) and its neighbour
-        u32x4_t p = *(const __attribute__((address_space(3))) u32x4_t*)(smem + c * 512u + ((q ^ (sw >> 1)) << 4));
-        if (sw & 1u) p = u32x4_t{p.z, p.w, p.x, p.y};
-        const unsigned o = (unsigned)row0 + 8u * q < ld_t ? (c * ld_t + (unsigned)row0 + 8u * q) * 2u : kOob;
-        __builtin_amdgcn_raw_buffer_store_b128(p, rt, (int)o, 0, 0);
-      }
-      // the row-major copy through the same LDS: every lane writes its kept dwords
-      // (two columns of one row) into a row-major 256×256 bf16 tile whose 16-byte
-      // pieces are XOR-swizzled by row_swz, then 16-byte pieces of whole rows go out
-      __syncthreads();
+    if constexpr (kStage) {
+      // the copy through LDS (free since the contraction's last barrier): every
+      // lane writes its kept dwords (two columns of one row) into a row-major
+      // 256×256 bf16 tile whose 16-byte pieces are XOR-swizzled by row_swz, then
+      // 16-byte pieces of whole rows go out
 #pragma unroll
       for (int blk = 0; blk < 8; ++blk) {
         const unsigned i = (unsigned)blk >> 1, j = (unsigned)blk & 1;
@@ -1176,6 +1235,7 @@ __global__ __launch_bounds__(kGemmThreads) void k_gemm(LaunchTable tab, LaunchSc
   extern __shared__ __align__(16) char smem[];
   __shared__ float red[kGemmWaves];
   constexpr int kElemsPerRow = kRowBytes / (int)sizeof(T);
+  constexpr bool kKmaj = sizeof(T) == 2;     // bf16: one storage-layout copy of X, K-major reads
   const int bid = xcd_logical_block();
   const int p = find_prob(tab.wg_prefix + PH * (tab.n_probs + 1), tab.n_probs, bid);
   const DevProblem& P = tab.probs[p];
@@ -1183,6 +1243,7 @@ __global__ __launch_bounds__(kGemmThreads) void k_gemm(LaunchTable tab, LaunchSc
   const int m = P.m;
 
   Operands op;
+  op.cola_b = op.colb_b = 0;
   int slice, row0, col0, ti = 0, tj = 0, u;
   if (PH == PH_GRAM || PH == PH_SQUARE) {
     const int T_ = P.tiles_m;
@@ -1201,6 +1262,27 @@ __global__ __launch_bounds__(kGemmThreads) void k_gemm(LaunchTable tab, LaunchSc
     op.rows_a = m - row0;
     op.rows_b = m - col0;
     op.ktiles = ld / kElemsPerRow;
+    if constexpr (kKmaj) {
+      if (PH == PH_GRAM) {
+        // X in storage layout: a wide slice's rows are rows of X (row-major
+        // operands), a tall slice's rows are its columns (K-major operands)
+        const int ld_s = P.wide ? P.ld_n : P.ld_m;
+        const T* xs = (const T*)P.xs[s.t & 1] + (int64_t)slice * P.rows * ld_s;
+        op.a = (const char*)(P.wide ? xs + (int64_t)row0 * ld_s : xs);
+        op.b = (const char*)(P.wide ? xs + (int64_t)col0 * ld_s : xs);
+        op.lda_b = op.ldb_b = ld_s * (int)sizeof(T);
+        if (!P.wide) {
+          op.rows_a = op.rows_b = P.rows;
+          op.cola_b = row0 * (int)sizeof(T);
+          op.colb_b = col0 * (int)sizeof(T);
+        }
+      } else {
+        // A' is symmetric: its rows serve as the K-major B operand as well
+        op.b = (const char*)base;
+        op.colb_b = col0 * (int)sizeof(T);
+        op.rows_b = m;
+      }
+    }
   } else {  // PH_APPLY: bands along the short (m) side, see band_tile
     const int per = P.apply_tr * P.apply_tc;
     slice = local / per;
@@ -1212,15 +1294,34 @@ __global__ __launch_bounds__(kGemmThreads) void k_gemm(LaunchTable tab, LaunchSc
     row0 = tr * kTile;
     col0 = tc * kTile;
     const T* bp = (const T*)P.bp + (int64_t)slice * m * P.ld_m;
-    const T* xa = (const T*)((s.t & 1) ? P.xa1 : P.xa0) + (int64_t)slice * P.n * P.ld_m;
-    const T* pa = P.wide ? bp : xa;     // rows of the output = storage rows
-    const T* pb = P.wide ? xa : bp;     // cols of the output = storage cols
-    op.a = (const char*)(pa + (int64_t)row0 * P.ld_m);
-    op.b = (const char*)(pb + (int64_t)col0 * P.ld_m);
-    op.lda_b = op.ldb_b = P.ld_m * (int)sizeof(T);
-    op.rows_a = P.rows - row0;
-    op.rows_b = P.cols - col0;
     op.ktiles = P.ld_m / kElemsPerRow;
+    op.lda_b = op.ldb_b = P.ld_m * (int)sizeof(T);
+    if constexpr (kKmaj) {
+      // wide: B′·X with X K-major (its storage rows are k); tall: S·B′ with the
+      // storage rows of S row-major and B′ (symmetric) K-major
+      const T* xs = (const T*)P.xs[s.t & 1] + (int64_t)slice * P.rows * (P.wide ? P.ld_n : P.ld_m);
+      op.colb_b = col0 * (int)sizeof(T);
+      if (P.wide) {
+        op.a = (const char*)(bp + (int64_t)row0 * P.ld_m);
+        op.b = (const char*)xs;
+        op.ldb_b = P.ld_n * (int)sizeof(T);
+        op.rows_a = P.rows - row0;
+        op.rows_b = P.rows;
+      } else {
+        op.a = (const char*)(xs + (int64_t)row0 * P.ld_m);
+        op.b = (const char*)bp;
+        op.rows_a = P.rows - row0;
+        op.rows_b = m;
+      }
+    } else {
+      const T* xa = (const T*)((s.t & 1) ? P.xa1 : P.xa0) + (int64_t)slice * P.n * P.ld_m;
+      const T* pa = P.wide ? bp : xa;     // rows of the output = storage rows
+      const T* pb = P.wide ? xa : bp;     // cols of the output = storage cols
+      op.a = (const char*)(pa + (int64_t)row0 * P.ld_m);
+      op.b = (const char*)(pb + (int64_t)col0 * P.ld_m);
+      op.rows_a = P.rows - row0;
+      op.rows_b = P.cols - col0;
+    }
   }
   float* scal = tab.scal + (int64_t)(P.slice_base + slice) * kScalStride;
 
@@ -1242,10 +1343,18 @@ __global__ __launch_bounds__(kGemmThreads) void k_gemm(LaunchTable tab, LaunchSc
   if constexpr (PH == PH_APPLY) {
     ApplyEpilogue<T, LAST> epi(P, s, slice, u, row0, col0);
     epi.prefetch();
-    gemm_mainloop<T>(op, smem, acc);
+    if constexpr (kKmaj) gemm_mainloop<T, false, true>(op, smem, acc);
+    else gemm_mainloop<T>(op, smem, acc);
     epi.finish(P, s, acc, slice, u, d, xs, smem, red);
   } else {
-    gemm_mainloop<T>(op, smem, acc);
+    if constexpr (!kKmaj) {
+      gemm_mainloop<T>(op, smem, acc);
+    } else if constexpr (PH == PH_SQUARE) {
+      gemm_mainloop<T, false, true>(op, smem, acc);
+    } else {
+      if (P.wide) gemm_mainloop<T, false, false>(op, smem, acc);
+      else gemm_mainloop<T, true, true>(op, smem, acc);
+    }
     sym_epilogue<T, PH>(P, s, acc, smem, slice, ti, tj, row0, col0, d, xs);
   }
 }
@@ -1272,6 +1381,7 @@ __global__ __launch_bounds__(kGemmThreads) void k_gemm_plain(GemmArgs g) {
   op.ldb_b = (int)(g.ldb * (int64_t)sizeof(T));
   op.rows_a = (int)(g.M - row0);
   op.rows_b = (int)(g.N - col0);
+  op.cola_b = op.colb_b = 0;
   op.ktiles = g.ktiles;
   f32x16_t acc[4][2];
   gemm_mainloop<T>(op, smem, acc);
