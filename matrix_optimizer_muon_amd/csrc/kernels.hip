@@ -472,10 +472,12 @@ __device__ __forceinline__ void buf_st(__amdgpu_buffer_rsrc_t r, unsigned off, u
 // (the NT stage moves 16 half lines); its MFMA fragments are read with the
 // transposing ds_read_b64_tr_b16 (two 8-byte reads per 16-byte fragment).  Its
 // 32-byte segments are XOR-swizzled by 2·(row & 3), which spreads the 8 rows × 2
-// segments one fragment read touches over all 64 banks.  K-major reads of a
-// bf16 operand were 5–16% faster than NT ones for the B operand of 2048- to
-// 8192-sized products, which is why symmetric operands (A′, B′) and the stored
-// X are read K-major wherever the product allows it.
+// segments one fragment read touches over all 64 banks.  A K-major B operand
+// made plain 2048- to 8192-sized products 5–16% faster than NT; with both
+// operands K-major (twice the fragment reads) it is about even.  On the bf16
+// path X is kept only in storage layout, so the apply reads X (wide) or the
+// symmetric B′ (tall) K-major and the tall Gram reads both operands K-major; the
+// square stays NT (measured faster there).
 //
 // Ping-pong schedule: the two waves sharing a SIMD belong to different groups
 // (group = wave >> 2, the 128-row half of the tile they own), and the groups run
@@ -1276,11 +1278,6 @@ __global__ __launch_bounds__(kGemmThreads) void k_gemm(LaunchTable tab, LaunchSc
           op.cola_b = row0 * (int)sizeof(T);
           op.colb_b = col0 * (int)sizeof(T);
         }
-      } else {
-        // A' is symmetric: its rows serve as the K-major B operand as well
-        op.b = (const char*)base;
-        op.colb_b = col0 * (int)sizeof(T);
-        op.rows_b = m;
       }
     }
   } else {  // PH_APPLY: bands along the short (m) side, see band_tile
@@ -1347,10 +1344,8 @@ __global__ __launch_bounds__(kGemmThreads) void k_gemm(LaunchTable tab, LaunchSc
     else gemm_mainloop<T>(op, smem, acc);
     epi.finish(P, s, acc, slice, u, d, xs, smem, red);
   } else {
-    if constexpr (!kKmaj) {
+    if constexpr (!kKmaj || PH == PH_SQUARE) {
       gemm_mainloop<T>(op, smem, acc);
-    } else if constexpr (PH == PH_SQUARE) {
-      gemm_mainloop<T, false, true>(op, smem, acc);
     } else {
       if (P.wide) gemm_mainloop<T, false, false>(op, smem, acc);
       else gemm_mainloop<T, true, true>(op, smem, acc);
