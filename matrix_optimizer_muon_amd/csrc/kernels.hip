@@ -125,13 +125,16 @@ __device__ __forceinline__ int stage_off(int r, int c) {
   return r * 1024 + ((((c >> 2) ^ ((r >> 3) & 15)) << 4) | ((c & 3) << 2));
 }
 
+// 4 consecutive elements of one source row, read once per step (gradient,
+// momentum): nontemporal loads, which measured faster here than plain ones
+typedef unsigned u32x2_nt __attribute__((ext_vector_type(2)));
 __device__ __forceinline__ void load4(const uint16_t* p, float (&v)[4]) {
-  const uint2 u = *(const uint2*)p;
+  const u32x2_nt u = __builtin_nontemporal_load((const u32x2_nt*)p);
   v[0] = __uint_as_float(u.x << 16); v[1] = __uint_as_float(u.x & 0xffff0000u);
   v[2] = __uint_as_float(u.y << 16); v[3] = __uint_as_float(u.y & 0xffff0000u);
 }
 __device__ __forceinline__ void load4(const float* p, float (&v)[4]) {
-  const float4 u = *(const float4*)p;
+  const f32x4_t u = __builtin_nontemporal_load((const f32x4_t*)p);
   v[0] = u.x; v[1] = u.y; v[2] = u.z; v[3] = u.w;
 }
 
