@@ -13,7 +13,7 @@ Follows the DMuon "架构设计" (Architecture design) page, §3.1 "分区（全
 * the LPT quality bound 4/3 − 1/(3R) and the per-layer counter-example
   (R = 8 slots, 7 matrices per layer leaves one slot idle every layer).
 
-Readings where the page is silent (also in the design doc):
+Readings where the page is silent:
 * cost = element count (cost_kind 0) or the NS flop count batch·(4m²n + 2m³)
   (cost_kind 1);
 * units are visited in a stable sort by cost, largest first, ties in input

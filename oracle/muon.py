@@ -21,8 +21,8 @@ What it follows
   than two dims act on their last two dims), §4.1 (``_validate_param_ndim``
   raises ``ValueError`` for fewer than two dims).
 
-Readings taken where the pages are silent (all also listed in the design doc)
------------------------------------------------------------------------
+Readings taken where the pages are silent
+-----------------------------------------
 * Momentum is plain heavy-ball B ← μB + G with no dampening and no Nesterov
   term; NS runs on the updated B.
 * Normalisation is X₀ = B / (‖B‖_F + eps) per 2-D slice (per expert for 3-D
