@@ -926,7 +926,7 @@ typedef unsigned u32x2_t __attribute__((ext_vector_type(2)));
 // reads) stores the row-major and the transposed copy directly.
 template <typename T, bool LAST>
 struct ApplyEpilogue {
-  static constexpr int kAhead = LAST ? 2 : 3;
+  static constexpr int kAhead = LAST ? 2 : 4;
   static constexpr int kPre = LAST ? 1 : 3;       // blocks loaded before the contraction
   static constexpr unsigned E = sizeof(T);
   // dwords per 4 values of the stored iterate: 24-bit values on the bf16 path
@@ -1093,9 +1093,10 @@ struct ApplyEpilogue {
   __device__ __forceinline__ void finish(const DevProblem& P, const LaunchScalars& s, f32x16_t (&acc)[4][2],
                                          int slice, int u, float d, float xs, char* smem, float* red) {
     constexpr bool kStage = E == 2 && !LAST;
-    // bf16 copy (storage layout), staged through LDS after the block loop: the
-    // dword each lane would store per block and (quad rq, pair pe)
-    uint32_t keep[kStage ? 8 : 1][8];
+    // bf16 copy (storage layout): each block's dwords (two columns of one row)
+    // go into a row-major 256×256 bf16 tile in LDS (free since the contraction's
+    // last barrier), whose 16-byte pieces are XOR-swizzled by row_swz; whole rows
+    // go out after the block loop
     const unsigned lc0 = (unsigned)(((threadIdx.x >> 6) & 3) * 64 + (threadIdx.x & 31));
     const float alpha = s.a + s.b * d + s.c * d * d;
     float sq = 0.f;
@@ -1186,7 +1187,10 @@ struct ApplyEpilogue {
             for (int pe = 0; pe < 2; ++pe) {        // register pair (2pe, 2pe + 1)
               const float v0 = v[4 * rq + 2 * pe], v1 = v[4 * rq + 2 * pe + 1];
               const float got = swap_adjacent(odd ? v0 : v1);
-              keep[kStage ? blk : 0][2 * rq + pe] = odd ? pack_bf16x2(got, v1) : pack_bf16x2(v0, got);
+              const unsigned cb = ((lc0 + 32u * (unsigned)j) & ~1u) * 2u;   // byte of the column pair in its row
+              const unsigned r = lr0 + (odd ? 1u : 0u) + 32u * (unsigned)i + 8u * (unsigned)rq + 2u * (unsigned)pe;
+              *(__attribute__((address_space(3))) uint32_t*)(smem + r * 512u + ((((cb >> 4) ^ row_swz(r)) << 4) | (cb & 15u))) =
+                  odd ? pack_bf16x2(got, v1) : pack_bf16x2(v0, got);
             }
           } else {
 #pragma unroll
@@ -1204,23 +1208,7 @@ struct ApplyEpilogue {
       if (threadIdx.x == 0) P.part_apply[(int64_t)slice * P.apply_tr * P.apply_tc + u] = tot;
     }
     if constexpr (kStage) {
-      // the copy through LDS (free since the contraction's last barrier): every
-      // lane writes its kept dwords (two columns of one row) into a row-major
-      // 256×256 bf16 tile whose 16-byte pieces are XOR-swizzled by row_swz, then
-      // 16-byte pieces of whole rows go out
-#pragma unroll
-      for (int blk = 0; blk < 8; ++blk) {
-        const unsigned i = (unsigned)blk >> 1, j = (unsigned)blk & 1;
-        const unsigned cb = ((lc0 + 32u * j) & ~1u) * 2u;           // byte of the column pair in its row
-#pragma unroll
-        for (int rq = 0; rq < 4; ++rq)
-#pragma unroll
-          for (int pe = 0; pe < 2; ++pe) {
-            const unsigned r = lr0 + (odd ? 1u : 0u) + 32u * i + 8u * rq + 2u * pe;
-            *(__attribute__((address_space(3))) uint32_t*)(smem + r * 512u + ((((cb >> 4) ^ row_swz(r)) << 4) | (cb & 15u))) =
-                keep[blk][2 * rq + pe];
-          }
-      }
+      // the staged copy: 16-byte pieces of whole rows go out
       __syncthreads();
 #pragma unroll 4
       for (int k = 0; k < 16; ++k) {
