@@ -1099,6 +1099,9 @@ struct ApplyEpilogue {
     // go out after the block loop
     const unsigned lc0 = (unsigned)(((threadIdx.x >> 6) & 3) * 64 + (threadIdx.x & 31));
     const float alpha = s.a + s.b * d + s.c * d * d;
+    // the value's scale, zero for columns past the matrix (their accumulators
+    // hold finite values read past a row's end: the next row or padding)
+    const float xsj[2] = {colok[0] ? xs : 0.f, colok[1] ? xs : 0.f};
     float sq = 0.f;
 #pragma unroll
     for (int b = kPre; b < kAhead; ++b) load_blk(b, b);
@@ -1116,7 +1119,7 @@ struct ApplyEpilogue {
       // columns past the matrix are zero: a K-major operand can feed them values
       // read past a row's end, which must not reach Σ X'² or any store
 #pragma unroll
-      for (int r = 0; r < 16; ++r) v[r] = colok[j] ? xs * fmaf(alpha, v[r], acc[i][j][r]) : 0.f;
+      for (int r = 0; r < 16; ++r) v[r] = xsj[j] * fmaf(alpha, v[r], acc[i][j][r]);
       if (LAST) {
         float w[16];
         if (has_out) {
@@ -1184,13 +1187,11 @@ struct ApplyEpilogue {
         for (int rq = 0; rq < 4; ++rq) {
           if constexpr (E == 2) {
 #pragma unroll
-            for (int pe = 0; pe < 2; ++pe) {        // register pair (2pe, 2pe + 1)
-              const float v0 = v[4 * rq + 2 * pe], v1 = v[4 * rq + 2 * pe + 1];
-              const float got = swap_adjacent(odd ? v0 : v1);
-              const unsigned cb = ((lc0 + 32u * (unsigned)j) & ~1u) * 2u;   // byte of the column pair in its row
-              const unsigned r = lr0 + (odd ? 1u : 0u) + 32u * (unsigned)i + 8u * (unsigned)rq + 2u * (unsigned)pe;
-              *(__attribute__((address_space(3))) uint32_t*)(smem + r * 512u + ((((cb >> 4) ^ row_swz(r)) << 4) | (cb & 15u))) =
-                  odd ? pack_bf16x2(got, v1) : pack_bf16x2(v0, got);
+            for (int e = 0; e < 4; ++e) {           // one 16-bit value per row
+              const unsigned cb = (lc0 + 32u * (unsigned)j) * 2u;            // byte of the column in its row
+              const unsigned r = lr0 + 32u * (unsigned)i + 8u * (unsigned)rq + (unsigned)e;
+              *(__attribute__((address_space(3))) uint16_t*)(smem + r * 512u + ((((cb >> 4) ^ row_swz(r)) << 4) | (cb & 15u))) =
+                  f32_to_bf16(v[4 * rq + e]);
             }
           } else {
 #pragma unroll
