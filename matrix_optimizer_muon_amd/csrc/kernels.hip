@@ -905,7 +905,9 @@ typedef unsigned u32x2_t __attribute__((ext_vector_type(2)));
 // Lane (h, r32) of wave (wr, wc) holds, for block (i, j) and register r = 4·rq + e,
 // the element at tile row 128·wr + 32·i + 8·rq + 4·h + e and tile column
 // 64·wc + 32·j + r32.  Per block:
-//   X' = xs·(α·X + acc), α = a + b·d + c·d²; at t = 0 X is read from the
+//   X' = xs·(α·X + acc), α = a + b·d + c·d² (xs = 0 for columns past the
+//        matrix, whose accumulators hold finite values read past a row's end);
+//        at t = 0 X is read from the
 //        unscaled source x0 (B, storage layout, 4-byte accesses: each wave
 //        instruction covers two 128-byte row segments) and xs = inv, else xs = 1
 //        and X is the stored iterate, kept in the order of the registers (16-byte
@@ -913,15 +915,15 @@ typedef unsigned u32x2_t __attribute__((ext_vector_type(2)));
 //        path 24-bit values (the top 24 bits of the fp32 value, rounded to
 //        nearest even), four per three dwords, so a block moves with 3 loads and
 //        3 stores; on the fp32 path fp32 values, 4 and 4
-//   t < k−1: the row-major operand copy, two columns per dword (even lanes take
-//        rows e = 0, 2 from their odd neighbour, odd lanes rows 1, 3), and the
-//        transposed copy; Σ X'² partial
-//   last:  W ← (1 − lr·wd)·W − lr·X', optional copy of X' to the output.
+//   t < k−1: the storage-layout operand copy (fp32 path: also the transposed
+//        copy); Σ X'² partial
+//   last:  W ← (1 − lr·wd)·W − lr·X', optional copy of X' to the output and
+//        bf16 copy of W (two columns per dword: even lanes take rows e = 0, 2
+//        from their odd neighbour, odd lanes rows 1, 3).
 // The bf16 copy of X' goes out through LDS (free once the contraction is done):
-// during the block loop each lane packs two columns of one row per dword (lane
-// exchange with its neighbour) and keeps the dwords; after the Σ X'² reduction
-// they are written into a row-swizzled 256×256 bf16 tile and stored as 16-byte
-// pieces of whole rows.  The bf16 path keeps only this storage-layout copy: every
+// during the block loop each lane writes its values as 16-bit bf16 into a
+// row-swizzled 256×256 tile; after the Σ X'² reduction the tile is stored as
+// 16-byte pieces of whole rows.  The bf16 path keeps only this storage-layout copy: every
 // bf16 contraction reads it row-major or K-major.  The fp32 path (no K-major
 // reads) stores the row-major and the transposed copy directly.
 template <typename T, bool LAST>
