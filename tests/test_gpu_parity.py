@@ -255,3 +255,20 @@ def test_stream_groups_do_not_change_results(monkeypatch):
     for other in runs[1:]:
         for (b0, o0, w0), (b1, o1, w1) in zip(runs[0], other):
             assert np.array_equal(b0, b1) and np.array_equal(o0, o1) and np.array_equal(w0, w1)
+
+
+@pytest.mark.parametrize("precision", ["bf16", "f32"])
+def test_longest_accepted_dims(precision):
+    """The longest side the library accepts (65536), wide and tall, batched."""
+    for shape in [(8, 65536), (65536, 8), (2, 3, 40000)]:
+        td = make_custom(shape, "f32", seed=(67, shape[-1]))
+        x = torch.from_numpy(td.grad.copy()).cuda()
+        out = mm.ns_batched(x, coeffs=Q5, steps=5, eps=HYPER["eps"], precision=precision)
+        torch.cuda.synchronize()
+        ref = oracle.newton_schulz_batched(td.grad, *Q5, 5, HYPER["eps"])
+        e = rel(out.cpu().numpy(), ref)
+        print(f"ns {shape} {precision}: {e:.2e}", flush=True)
+        assert e <= TOL_NS[precision], (shape, e)
+    tds = [make_custom((8, 65536), "bf16", seed=(67, 1), scale=1e-3),
+           make_custom((65536, 8), "f32", seed=(67, 2))]
+    check_step(tds, precision, label="longest dims")
