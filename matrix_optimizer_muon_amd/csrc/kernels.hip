@@ -125,6 +125,15 @@ __device__ __forceinline__ int stage_off(int r, int c) {
   return r * 1024 + ((((c >> 2) ^ ((r >> 3) & 15)) << 4) | ((c & 3) << 2));
 }
 
+// The same half-tile for the square's epilogue, which reads 8 columns per lane:
+// chunks XOR-swizzled by (r >> 3) & 15 as above, and chunk k's bit 0 flipped when bit 4 of k is
+// set, so that the even (or the odd) chunks of a row, which one instruction of
+// the row pass reads (8 columns per lane), fall in 16 different bank groups.
+__device__ __forceinline__ int stage_off8(int r, int c) {
+  const int k = c >> 2;
+  return r * 1024 + (((k ^ ((k >> 4) & 1) ^ ((r >> 3) & 15)) << 4) | ((c & 3) << 2));
+}
+
 // 4 consecutive elements of one source row, read once per step (gradient,
 // momentum): nontemporal loads, which measured faster here than plain ones
 typedef unsigned u32x2_nt __attribute__((ext_vector_type(2)));
@@ -894,6 +903,101 @@ __device__ __forceinline__ void sym_epilogue(const DevProblem& P, const LaunchSc
   }
 }
 
+// ---- square epilogue on the bf16 path: B' = (b + 2cd)·A' + c·acc, as in
+// sym_epilogue, but the row pass takes 8 columns per lane and chunk (16-byte
+// loads of A' and 16-byte stores of B'), and each half's A' values are loaded
+// one step early (the first half's before its staging, the second half's after
+// the first half's row pass), so their latency overlaps the staging, the column
+// pass and the barriers instead of stalling the row pass.
+template <typename T>
+__device__ __forceinline__ void square_epilogue(const DevProblem& P, const LaunchScalars& s,
+                                                f32x16_t (&acc)[4][2], char* smem, int slice, int ti,
+                                                int tj, int row0, int col0, float d) {
+  static_assert(sizeof(T) == 2, "bf16 path");
+  const int tid = threadIdx.x;
+  const int m = P.m, ldm = P.ld_m;
+  T* dst = (T*)P.bp + (int64_t)slice * m * ldm;
+  T* dstT = ti != tj ? dst : nullptr;
+  const T* aprime = (const T*)P.ap + (int64_t)slice * m * ldm;
+  const float lin = s.b + 2.f * s.c * d;
+  const int lane = tid & 63, wave = tid >> 6;
+  const int wr = wave >> 2, wc = wave & 3, h = lane >> 5, r32 = lane & 31;
+  // row pass: 128 rows × 32 chunks of 8 columns per half, 8 chunks per thread;
+  // chunk q of this thread: row (tid + 512q) / 32, columns 8·((tid + 512q) % 32)
+  constexpr int kQ = 8;
+  u32x4_t ain[kQ];
+  auto load_ap = [&](int hf) {
+#pragma unroll
+    for (int q = 0; q < kQ; ++q) {
+      const int id = tid + kGemmThreads * q;
+      const int gr = row0 + hf * 128 + (id >> 5), gc = col0 + 8 * (id & 31);
+      ain[q] = gr < m && gc < ldm ? *(const u32x4_t*)(aprime + (int64_t)gr * ldm + gc)
+                                  : u32x4_t{0u, 0u, 0u, 0u};
+    }
+  };
+  load_ap(0);
+#pragma unroll
+  for (int hf = 0; hf < 2; ++hf) {
+    // (1) the four waves holding rows [128·hf, 128·hf + 128) stage their accumulators
+    if (wr == hf) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int rr = i * 32 + (r >> 2) * 8 + h * 4 + (r & 3);
+            const int cc = wc * 64 + j * 32 + r32;
+            *(float*)(smem + stage_off8(rr, cc)) = acc[i][j][r];
+          }
+    }
+    __syncthreads();
+    // (2) row pass
+#pragma unroll
+    for (int q = 0; q < kQ; ++q) {
+      const int id = tid + kGemmThreads * q;
+      const int rr = id >> 5, c8 = id & 31;
+      float* sp0 = (float*)(smem + stage_off8(rr, 8 * c8));
+      float* sp1 = (float*)(smem + stage_off8(rr, 8 * c8 + 4));
+      const float4 a0 = *(const float4*)sp0, a1 = *(const float4*)sp1;
+      const float c_[8] = {a0.x, a0.y, a0.z, a0.w, a1.x, a1.y, a1.z, a1.w};
+      const uint32_t w[4] = {ain[q].x, ain[q].y, ain[q].z, ain[q].w};
+      float v[8];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        v[2 * e] = fmaf(lin, __uint_as_float(w[e] << 16), s.c * c_[2 * e]);
+        v[2 * e + 1] = fmaf(lin, __uint_as_float(w[e] & 0xffff0000u), s.c * c_[2 * e + 1]);
+      }
+      const int gr = row0 + hf * 128 + rr, gc = col0 + 8 * c8;
+      if (gr < m && gc < ldm) store_row16(dst + (int64_t)gr * ldm + gc, v);
+      if (dstT) {
+        *(float4*)sp0 = make_float4(v[0], v[1], v[2], v[3]);
+        *(float4*)sp1 = make_float4(v[4], v[5], v[6], v[7]);
+      }
+    }
+    if (hf == 0) load_ap(1);
+    __syncthreads();
+    // (3) column pass: rows of the mirrored block = tile columns
+    if (dstT) {
+      constexpr int RPC = 8;                            // rows per 16-byte chunk
+      constexpr int CPC = 128 / RPC;                    // chunks per column (this half)
+#pragma unroll 2
+      for (int k = 0; k < (256 * CPC) / kGemmThreads; ++k) {
+        const int id = tid + kGemmThreads * k;
+        const int cc = id / CPC, rg = id % CPC;
+        const int trow = col0 + cc;
+        const int tcol = row0 + hf * 128 + rg * RPC;
+        if (trow >= m || tcol >= ldm) continue;
+        float v[RPC];
+#pragma unroll
+        for (int e = 0; e < RPC; ++e) v[e] = *(const float*)(smem + stage_off8(rg * RPC + e, cc));
+        store_row16(dstT + (int64_t)trow * ldm + tcol, v);
+      }
+    }
+    __syncthreads();
+  }
+}
+
 // value of the neighbouring lane (lane ^ 1)
 __device__ __forceinline__ float swap_adjacent(float x) {
   return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0xB1, 0xF, 0xF, false));
@@ -1344,7 +1448,8 @@ __global__ __launch_bounds__(kGemmThreads) void k_gemm(LaunchTable tab, LaunchSc
       if (P.wide) gemm_mainloop<T, false, false>(op, smem, acc);
       else gemm_mainloop<T, true, true>(op, smem, acc);
     }
-    sym_epilogue<T, PH>(P, s, acc, smem, slice, ti, tj, row0, col0, d, xs);
+    if constexpr (PH == PH_SQUARE && sizeof(T) == 2) square_epilogue<T>(P, s, acc, smem, slice, ti, tj, row0, col0, d);
+    else sym_epilogue<T, PH>(P, s, acc, smem, slice, ti, tj, row0, col0, d, xs);
   }
 }
 
