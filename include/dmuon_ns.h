@@ -35,11 +35,16 @@
  *   every buffer alive until that work completes.
  * - The caller owns and frees all memory, including the workspace.  The library
  *   allocates no device memory.  Between calls it keeps only the opt-in
- *   phase-timing events (dmuon_phase_timing) and eight pinned host buffers
- *   (with one event each) through which a call stages its tensor table to the
- *   workspace, so that the host need not wait for the stream.
+ *   phase-timing events (dmuon_phase_timing), eight pinned host buffers (with
+ *   one event each) through which a call stages its tensor table to the
+ *   workspace, so that the host need not wait for the stream, and, per device,
+ *   the three streams (default priority) and four events with which a step
+ *   split into concurrent groups forks from and joins back to `stream`.
  * - Every argument is validated on the host, before anything is enqueued, so a
  *   rejected call leaves all buffers untouched.  Validation makes no HIP call.
+ * - The staged table copy reads a pinned buffer that later calls reuse, so it
+ *   must not be replayed from a HIP graph: a call on a stream that is capturing
+ *   a graph returns DMUON_E_HIP before enqueuing anything.
  * - Return value: DMUON_OK or a negative DMUON_E_* code; dmuon_last_error()
  *   then gives a message (thread-local, valid until the next call on the thread).
  * - After DMUON_E_HIP (a HIP launch/copy failed after validation) the contents

@@ -485,6 +485,18 @@ static int check_workspace(void* ws, size_t have, size_t need) {
   return DMUON_OK;
 }
 
+// The table copy reads a pinned staging buffer that later calls reuse: captured
+// into a graph, its replays would read whatever that buffer then holds.
+static int refuse_capture(void* stream) {
+  hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+  const hipError_t e = hipStreamIsCapturing((hipStream_t)stream, &cs);
+  if (e != hipSuccess) return fail(DMUON_E_HIP, std::string("stream query: ") + hip_error_string((int)e));
+  if (cs != hipStreamCaptureStatusNone)
+    return fail(DMUON_E_HIP, "the stream is capturing a graph: the step stages its tables through a reused "
+                             "host buffer and cannot be captured");
+  return DMUON_OK;
+}
+
 static int test_fail_hook() {
   // DMUON_TEST_FAIL_AT=plan makes a valid call fail as a HIP error would, before
   // anything is enqueued (used by the host-side failure tests).
@@ -617,6 +629,7 @@ int dmuon_muon_step(const dmuon_tensor* tensors, int32_t n, const dmuon_step_cfg
   for (const Range& r : rs)
     if (r.lo < whi && wlo < r.hi) return fail(DMUON_E_ALIAS, "workspace overlaps a tensor buffer");
   if ((e = test_fail_hook())) return e;
+  if ((e = refuse_capture(stream))) return e;
   GroupPlan real;
   if ((e = plan_groups(items, f32, (char*)workspace, real))) return e;
   LaunchScalars s{};
@@ -683,6 +696,7 @@ int dmuon_ns_batched(const void* x, int32_t x_dtype, float* out, int64_t batch, 
   for (const Range& r : rs)
     if (r.lo < whi && wlo < r.hi) return fail(DMUON_E_ALIAS, "workspace overlaps x or out");
   if ((e = test_fail_hook())) return e;
+  if ((e = refuse_capture(stream))) return e;
   Plan real;
   if ((e = build_plan(items, f32, real, (char*)workspace))) return e;
   LaunchScalars s{};
@@ -726,6 +740,7 @@ int dmuon_adamw_step(const dmuon_adamw_tensor* tensors, int32_t n, const dmuon_a
   for (const Range& r : rs)
     if (r.lo < whi && wlo < r.hi) return fail(DMUON_E_ALIAS, "workspace overlaps a tensor buffer");
   if ((e = test_fail_hook())) return e;
+  if ((e = refuse_capture(stream))) return e;
   std::vector<char> host(pl.bytes, 0);
   std::memcpy(host.data(), pl.probs.data(), pl.probs.size() * sizeof(AdamwProblem));
   std::memcpy(host.data() + pl.off_prefix, pl.prefix.data(), pl.prefix.size() * sizeof(int32_t));

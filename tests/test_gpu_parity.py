@@ -272,3 +272,18 @@ def test_longest_accepted_dims(precision):
     tds = [make_custom((8, 65536), "bf16", seed=(67, 1), scale=1e-3),
            make_custom((65536, 8), "f32", seed=(67, 2))]
     check_step(tds, precision, label="longest dims")
+
+
+def test_graph_capture_is_refused():
+    """A call on a stream that is capturing a graph is rejected before it enqueues
+    anything (its table copy reads a reused host buffer), and the capture and the
+    next plain call are unaffected."""
+    td = make_custom((300, 700), "f32", seed=(68, 0))
+    g_, m_, w_ = to_dev(td)
+    graph = torch.cuda.CUDAGraph()
+    with pytest.raises(RuntimeError, match="capturing a graph"):
+        with torch.cuda.graph(graph):
+            mm.muon_step([g_], [m_], [w_])
+    torch.cuda.synchronize()
+    assert np.array_equal(m_.cpu().numpy(), td.momentum) and np.array_equal(w_.cpu().numpy(), td.master)
+    check_step([td], "bf16", label="after refused capture")
