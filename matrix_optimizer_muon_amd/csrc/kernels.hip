@@ -1269,8 +1269,9 @@ struct ApplyEpilogue {
           pack24(v, w);
 #pragma unroll
           for (int q = 0; q < 3; ++q)
+            // nontemporal (cache policy 2): read again only by the next apply
             __builtin_amdgcn_raw_buffer_store_b128(u32x4_t{w[4 * q], w[4 * q + 1], w[4 * q + 2], w[4 * q + 3]}, rx,
-                                                   (int)xq(blk, q), 0, 0);
+                                                   (int)xq(blk, q), 0, 2);
         } else {
 #pragma unroll
           for (int rq = 0; rq < 4; ++rq)
@@ -1324,7 +1325,7 @@ struct ApplyEpilogue {
         const u32x4_t p = *(const __attribute__((address_space(3))) u32x4_t*)(smem + r * 512u + ((q ^ row_swz(r)) << 4));
         const unsigned c = (unsigned)col0 + 8u * q;
         const unsigned o = c < ld_s ? (r * ld_s + c) * 2u : kOob;
-        __builtin_amdgcn_raw_buffer_store_b128(p, rd, (int)o, 0, 0);
+        __builtin_amdgcn_raw_buffer_store_b128(p, rd, (int)o, 0, 2);   // nontemporal
       }
     }
   }
