@@ -1170,7 +1170,7 @@ struct ApplyEpilogue {
     } else {
 #pragma unroll
       for (int q = 0; q < kXWords; ++q) {
-        const f32x4_t w = __builtin_amdgcn_raw_buffer_load_b128(rx, (int)xq(blk, q), 0, 0);
+        const f32x4_t w = __builtin_amdgcn_raw_buffer_load_b128(rx, (int)xq(blk, q), 0, 2);   // nontemporal
         xin[slot][4 * q] = w.x; xin[slot][4 * q + 1] = w.y;
         xin[slot][4 * q + 2] = w.z; xin[slot][4 * q + 3] = w.w;
       }
@@ -1179,7 +1179,8 @@ struct ApplyEpilogue {
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const unsigned rr = (unsigned)(32 * i + 8 * (r >> 2) + (r & 3));
-        win[LAST ? slot : 0][r] = buf_ld(rw, wo[j] + rr * cols * 4u);
+        // the master weight is read and written once per step: nontemporal
+        win[LAST ? slot : 0][r] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rw, (int)(wo[j] + rr * cols * 4u), 0, 2));
       }
     }
   }
@@ -1240,7 +1241,7 @@ struct ApplyEpilogue {
           for (int r = 0; r < 16; ++r) {
             const unsigned rr = (unsigned)(32 * i + 8 * (r >> 2) + (r & 3));
             w[r] = fmaf(-s.lr, v[r], s.decay * win[LAST ? slot : 0][r]);
-            buf_st(rw, wo[j] + rr * cols * 4u, w[r]);
+            __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(w[r]), rw, (int)(wo[j] + rr * cols * 4u), 0, 2);
           }
         }
         if (!has_pub) {
