@@ -931,7 +931,7 @@ __device__ __forceinline__ void square_epilogue(const DevProblem& P, const Launc
     for (int q = 0; q < kQ; ++q) {
       const int id = tid + kGemmThreads * q;
       const int gr = row0 + hf * 128 + (id >> 5), gc = col0 + 8 * (id & 31);
-      ain[q] = gr < m && gc < ldm ? *(const u32x4_t*)(aprime + (int64_t)gr * ldm + gc)
+      ain[q] = gr < m && gc < ldm ? __builtin_nontemporal_load((const u32x4_t*)(aprime + (int64_t)gr * ldm + gc))  // last read of A'
                                   : u32x4_t{0u, 0u, 0u, 0u};
     }
   };
@@ -1165,7 +1165,7 @@ struct ApplyEpilogue {
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const unsigned rr = (unsigned)(32 * i + 8 * (r >> 2) + (r & 3));
-        xin[slot][r] = buf_ld(ri, xi[j] + rr * ldi * 4u);
+        xin[slot][r] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(ri, (int)(xi[j] + rr * ldi * 4u), 0, 2));  // nt
       }
     } else {
 #pragma unroll
