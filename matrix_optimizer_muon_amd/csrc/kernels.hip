@@ -731,7 +731,7 @@ __device__ __forceinline__ int acc_col(int j) {
   return (wave & 3) * 64 + j * 32 + (lane & 31);
 }
 
-// Tile orders.  Consecutive logical tiles run on one XCD in runs of kXcdRun (see
+// Tile orders.  Consecutive logical tiles run on one XCD in runs of 16 or 32 (see
 // xcd_logical_block), so the order decides how many operand panels one XCD's L2
 // has to hold at once.  Both orders walk bands of kBand tiles along one side of
 // the output and advance the other side every kBand tiles, so a run of 32 tiles
@@ -780,19 +780,21 @@ __device__ __forceinline__ void tri_tile(int u, int T, int& ti, int& tj) {
 
 // Logical workgroup index.  Workgroups are handed to the 8 XCDs round-robin in
 // launch order, so workgroup b runs on XCD b % 8 as its (b / 8)-th workgroup.
-// The logical tile list is consumed in windows of 8·kXcdRun tiles: inside a
-// window each XCD takes kXcdRun consecutive tiles (neighbours share operand
-// panels in that XCD's L2), and all XCDs advance through the list together, so
-// tiles of unequal cost (long-K problems first) are spread over every XCD.  A
-// last partial window of R tiles is split the same way into 8 contiguous runs
-// (the first R % 8 XCDs take one tile more).  The map is a bijection on [0, G).
-constexpr int kXcdRun = 32;
+// The logical tile list is consumed in windows of 8·RUN tiles: inside a window
+// each XCD takes RUN consecutive tiles (neighbours share operand panels in that
+// XCD's L2), and all XCDs advance through the list together, so tiles of
+// unequal cost (long-K problems first) are spread over every XCD.  A last
+// partial window of R tiles is split the same way into 8 contiguous runs (the
+// first R % 8 XCDs take one tile more).  The map is a bijection on [0, G).
+// Runs of 32 suit the square and the apply; the Gram, whose tiles read two
+// row panels of the same X, measured faster with runs of 16.
+template <int RUN>
 __device__ __forceinline__ int xcd_logical_block() {
   const int G = gridDim.x, b = blockIdx.x;
-  constexpr int win = 8 * kXcdRun;
+  constexpr int win = 8 * RUN;
   const int w = b / win;
-  const int xcd = b & 7, slot = (b >> 3) - w * kXcdRun;
-  if ((w + 1) * win <= G) return w * win + xcd * kXcdRun + slot;
+  const int xcd = b & 7, slot = (b >> 3) - w * RUN;
+  if ((w + 1) * win <= G) return w * win + xcd * RUN + slot;
   const int R = G - w * win, per = R >> 3, rem = R & 7;
   return w * win + (xcd < rem ? xcd * (per + 1) : rem * (per + 1) + (xcd - rem) * per) + slot;
 }
@@ -1338,7 +1340,7 @@ __global__ __launch_bounds__(kGemmThreads) void k_gemm(LaunchTable tab, LaunchSc
   __shared__ float red[kGemmWaves];
   constexpr int kElemsPerRow = kRowBytes / (int)sizeof(T);
   constexpr bool kKmaj = sizeof(T) == 2;     // bf16: one storage-layout copy of X, K-major reads
-  const int bid = xcd_logical_block();
+  const int bid = xcd_logical_block<PH == PH_GRAM ? 16 : 32>();
   const int p = find_prob(tab.wg_prefix + PH * (tab.n_probs + 1), tab.n_probs, bid);
   const DevProblem& P = tab.probs[p];
   const int local = bid - P.wg0[PH];
