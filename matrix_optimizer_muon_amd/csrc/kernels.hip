@@ -372,7 +372,7 @@ __global__ __launch_bounds__(kThreads) void k_adamw(AdamwTable tab, AdamwScalars
     // 8 elements per vector; each pass handles kVec vectors per thread and
     // issues all their loads before any store (the buffers may alias as far as
     // the compiler knows, so it would not move loads above earlier stores)
-    constexpr int kVec = 2;
+    constexpr int kVec = 4;
     const int64_t nvec = (e1 - e0) >> 3;
     auto load_vec = [&](int64_t e, float (&g)[8], float (&pv)[8], float (&mv)[8], float (&vw)[8]) {
       if (P.grad_bf16) {
