@@ -1007,20 +1007,21 @@ __device__ __forceinline__ float swap_adjacent(float x) {
 
 typedef unsigned u32x2_t __attribute__((ext_vector_type(2)));
 
-// ---- apply epilogue, in the accumulator layout (no LDS, no barrier, no branch).
+// ---- apply epilogue, in the accumulator layout.
 // Lane (h, r32) of wave (wr, wc) holds, for block (i, j) and register r = 4·rq + e,
 // the element at tile row 128·wr + 32·i + 8·rq + 4·h + e and tile column
 // 64·wc + 32·j + r32.  Per block:
 //   X' = xs·(α·X + acc), α = a + b·d + c·d² (xs = 0 for columns past the
-//        matrix, whose accumulators hold finite values read past a row's end);
-//        at t = 0 X is read from the
-//        unscaled source x0 (B, storage layout, 4-byte accesses: each wave
-//        instruction covers two 128-byte row segments) and xs = inv, else xs = 1
-//        and X is the stored iterate, kept in the order of the registers (16-byte
-//        pieces per lane, 1 KiB contiguous per wave instruction): on the bf16
-//        path 24-bit values (the top 24 bits of the fp32 value, rounded to
-//        nearest even), four per three dwords, so a block moves with 3 loads and
-//        3 stores; on the fp32 path fp32 values, 4 and 4
+//        matrix, whose accumulators hold finite values read past a row's end).
+//        At t = 0 X is read from the unscaled source x0 (B, storage layout,
+//        4-byte accesses: each wave instruction covers two 128-byte row
+//        segments) and xs = inv; later xs = 1 and X is the stored iterate, kept
+//        in the order of the registers (16-byte pieces per lane, 1 KiB
+//        contiguous per wave instruction): on the bf16 path 24-bit values (the
+//        top 24 bits of the fp32 value, rounded to nearest even), four per three
+//        dwords, so a block moves with 3 loads and 3 stores; on the fp32 path
+//        fp32 values, 4 and 4.  Traffic touched once per phase (the iterate, the
+//        copy, the master weight) uses the nontemporal cache policy.
 //   t < k−1: the storage-layout operand copy (fp32 path: also the transposed
 //        copy); Σ X'² partial
 //   last:  W ← (1 − lr·wd)·W − lr·X', optional copy of X' to the output and
