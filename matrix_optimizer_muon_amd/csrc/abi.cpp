@@ -286,12 +286,11 @@ constexpr int kMaxGroups = 4;
 // fixed count keeps the workspace size a host-only computation).  Measured, ms
 // per step with 1 / 2 / 3 / 4 groups:
 // * below 4 rounds: four groups, whose tail rounds and epilogues overlap each
-//   other's contractions (one d=2048 layer: 2.86 / 2.68 / 2.63 / 2.60);
+//   other's contractions (one d=2048 layer: 2.61 / 2.46 / 2.47 / 2.42);
 // * otherwise one: the tails are a small share, and one launch sequence keeps
 //   the operand panels of neighbouring tiles together in each XCD's L2 (Llama
-//   d=4096 share: 60.9 / 63.5; MLP/MoE mix of 8192-wide matrices and 1408-wide
-//   experts: 121.6 / 127.3 / 127.9 / 131.3; 384 small matrices: 3.12 / 3.10–3.72
-//   / 3.47–3.97).
+//   d=4096 share: 58.2 / 60.2; MLP/MoE mix of 8192-wide matrices and 1408-wide
+//   experts: 116.1 / 122.0; 384 small matrices: 2.74 / 2.76).
 constexpr int kCusAssumed = 256;
 
 static int group_count(const std::vector<Item>& items) {
