@@ -4,8 +4,8 @@
 // owner-local step) is run as one grouped launch per phase over every 2-D slice
 // of every tensor:
 //
-//   ingest     B ← μB + s·G, per-tile partial Σ B², and the operand copies of
-//              B (oriented row-major and its transpose, zero padded)
+//   ingest     B ← μB + s·G, per-tile partial Σ B², and the operand copy of B
+//              in storage layout, zero padded (fp32 path: also its transpose)
 //   norm       inv = 1/(‖B‖_F + eps), X₀ = inv·B (the scale is folded into the
 //              first Gram and the first apply)
 //   k × { gram    A' = X Xᵀ − d·I          (upper 256×256 tiles, mirrored)
@@ -19,11 +19,13 @@
 // bf16 rounding of A's large diagonal out of the result; the iterate itself
 // stays fp32.
 //
-// Every contraction is an "NT" product C[i][j] = Σ_k P[i][k]·Q[j][k] with both
-// operands K-contiguous (rows of a row-major matrix): the Gram uses the oriented
-// X (m×n) twice, the square uses the symmetric A' twice, and the apply uses B'
-// and the oriented transpose Xᵀ (n×m), ordered so that the output tile is in the
-// tensor's own storage layout.
+// Every contraction is C[i][j] = Σ_k P(i, k)·Q(j, k) on one core whose operands
+// are read row-major (K-contiguous) or K-major (see the core below): on the bf16
+// path the Gram reads X from its storage-layout copy (row-major for a wide slice,
+// K-major for a tall one), the square reads the symmetric A' twice row-major, and
+// the apply pairs B' with X so that the output tile is in the tensor's own
+// storage layout; the fp32 path keeps X in both orientations and reads every
+// operand row-major.
 #include <hip/hip_runtime.h>
 
 #include <cstdint>
