@@ -3,7 +3,7 @@
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--publish]
     python bench.py --route adamw [--workload adamw_stream|adamw_llama_norms]
 
-A step is one call of ``dmuon_muon_step`` over every matrix of the workload
+A step is one Muon step over every matrix of the workload
 (momentum, per-slice normalisation, k = 5 quintic Newton–Schulz iterations,
 decoupled decay + lr-scaled update), with all inputs already resident in HBM.
 Prints one JSON line.  ``value`` is matrices stepped per second; the line also
@@ -11,10 +11,13 @@ carries the effective TFLOP/s (Σ k·(4m²n + 2m³) per step), its share of the 
 dense matrix-core peak, a roofline entry for the dominant kernel and the fp64 CPU
 oracle timed on a bounded sample of the same workload.
 
-The step is timed twice.  The first timed pass gives ``value``: the library's own
-launch configuration (it may split the tensors into concurrent stream groups),
-no per-launch events.  The second pass runs the same kernels on one stream
-(``DMUON_STREAM_GROUPS=1``) with HIP events around every launch on that stream;
+A step is prepared once (``dmuon_muon_step_prepare`` writes the tables for the
+workload's tensors into the workspace) and every timed step is one
+``dmuon_muon_step_run``.  The step is timed twice.  The first timed pass gives
+``value``: the library's own launch configuration (it may split the tensors into
+concurrent stream groups on side streams), no per-launch events.  The second pass
+runs the same kernels on one stream (``stream_groups`` = 1) with HIP events
+around every launch on that stream;
 the roofline and the per-phase times come from it, because the duration of a
 launch that shares the GPU with another stream's kernels says nothing about
 the kernel itself.  ``--stream-groups N`` fixes the group count of the first
@@ -40,7 +43,7 @@ sys.path.insert(0, ROOT)
 
 PEAK_BF16_TFLOPS = 2500.0     # MI355X dense bf16 matrix-core peak (published)
 PEAK_HBM_GBS = 8000.0         # MI355X HBM3E (published)
-DEFAULT_WORKLOAD = "layer_d2048"
+DEFAULT_WORKLOAD = "mlp_moe_large"
 METRIC = "Muon NS step matrices/s + TFLOP/s and % bf16 MFMA peak, 1\u00d7MI355X"
 ADAMW_METRIC = "adamw route elements/s (owner 1-D parameters), 1\u00d7MI355X"
 ADAMW_DEFAULT_WORKLOAD = "adamw_stream"
@@ -94,6 +97,35 @@ def copy_probe(nbytes):
     print(json.dumps({"copy_probe_bytes": nbytes}), flush=True)
 
 
+def copy_ceiling_gbs(nbytes=1 << 30, reps=10):
+    """Bytes per second (read + write) of a plain 1 GiB device-to-device copy,
+    timed with HIP events: the practical ceiling of a kernel that writes as
+    much as it reads."""
+    import torch
+    src = torch.empty(nbytes // 4, dtype=torch.float32, device="cuda").fill_(1.0)
+    dst = torch.empty_like(src)
+    for _ in range(2):
+        dst.copy_(src)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        dst.copy_(src)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / reps
+    del src, dst
+    return 2 * nbytes / (ms * 1e-3) / 1e9
+
+
+def ingest_bytes_per_elem(grad_dtype, precision):
+    """(algorithmic, moved) HBM bytes per element of the momentum kernel: the
+    gradient read, the momentum read and written; it also writes the first
+    iteration's operand copy of B (bf16, or fp32 in both orientations on the
+    fp32 path)."""
+    alg = (2 if grad_dtype == "bf16" else 4) + 8
+    return alg, alg + (2 if precision == "bf16" else 8)
+
+
 def matrices_of(wl, share=None):
     """(rows, cols, batch) of every stepped slice group."""
     ts = wl.tensors if share is None else [wl.tensors[i] for i in share]
@@ -140,45 +172,86 @@ def select_share(wl_name):
     return wl, [int(i) for i in res["owner_order"]]
 
 
-def cpu_baseline(wl, ts, budget_s=20.0, min_s=10.0, max_passes=8):
-    """fp64 oracle on a bounded sample of the workload, scaled to matrices/s.
-
-    The sample is whole tensors in workload order up to an estimated budget_s of
-    work; passes over it repeat until min_s of measured oracle time (at most
-    max_passes), so that small workloads are timed over seconds, not a blink."""
-    import oracle
-    from matrix_optimizer_muon_amd.workloads import HYPER, make_tensor
+def blas_threads():
     try:
         from threadpoolctl import threadpool_info
-        threads = max([p.get("num_threads", 1) for p in threadpool_info()
-                       if p.get("user_api") == "blas"] or [1])
+        return max([p.get("num_threads", 1) for p in threadpool_info()
+                    if p.get("user_api") == "blas"] or [1])
     except Exception:  # pragma: no cover
-        threads = os.cpu_count() or 1
-    # sample: whole tensors in workload order until the flop budget estimate is used
-    est_rate = 2.0e11     # fp64 flop/s assumed for the sample size only
-    chosen, fl = [], 0
+        return os.cpu_count() or 1
+
+
+def slice_shapes(ts):
+    """Distinct (rows, cols, grad dtype) of the stepped 2-D slices, with counts,
+    in workload order, each with the first tensor holding it."""
+    out = {}
     for t in ts:
-        f = ns_flops([t], HYPER["steps"])
-        if chosen and (fl + f) / est_rate > budget_s:
-            break
-        chosen.append(t)
-        fl += f
-    # time only the oracle calls, not the input generation
-    total, passes = 0.0, 0
-    while passes < max_passes and (passes == 0 or total < min_s):
-        for t in chosen:
-            td = make_tensor(wl, t)
-            t1 = time.perf_counter()
-            oracle.muon_step(td.grad, td.momentum, td.master, lr=HYPER["lr"], mu=HYPER["mu"],
-                             wd=HYPER["wd"], eps=HYPER["eps"], a=HYPER["a"], b=HYPER["b"],
-                             c=HYPER["c"], steps=HYPER["steps"])
-            total += time.perf_counter() - t1
-        passes += 1
-    slices = n_slices(chosen) * passes
-    return {"value": slices / total, "unit": "matrices/s", "cores": int(threads), "kind": "oracle",
-            "sample": f"{len(chosen)} of {len(ts)} tensors ({n_slices(chosen)} matrices) of the workload, "
-                      f"one full step each in fp64 numpy, {passes} pass(es), {total:.2f} s",
-            "seconds": total, "gflops_fp64": ns_flops(chosen, HYPER["steps"]) * passes / total / 1e9}
+        key = (tuple(t.shape[-2:]), t.grad_dtype)
+        b = t.shape[0] if len(t.shape) == 3 else 1
+        if key not in out:
+            out[key] = [t, 0]
+        out[key][1] += b
+    return [(key, spec, count) for key, (spec, count) in out.items()]
+
+
+def cpu_baseline(wl, ts, budget_s=25.0, min_s=10.0, max_passes=64, est_rate=4.0e11):
+    """fp64 oracle on one 2-D slice of every distinct slice shape, scaled by count.
+
+    Each slice gets one full step (momentum, normalisation, k Newton–Schulz
+    iterations, decay + update) of the oracle as it stands.  A slice whose step
+    is estimated (at ``est_rate`` flop/s) above its share of ``budget_s`` is
+    instead stepped at k = 0 and at k = 1 and its k-step time taken as
+    t0 + k·(t1 − t0) (the iterations all cost the same).  Whole-step slices are
+    repeated until ``min_s`` of measured time (at most ``max_passes``).  The
+    workload's step time is Σ count·t_slice; the value is its slices per second."""
+    import numpy as np
+    import oracle
+    from matrix_optimizer_muon_amd.workloads import HYPER, make_tensor
+
+    k = HYPER["steps"]
+    hp = dict(lr=HYPER["lr"], mu=HYPER["mu"], wd=HYPER["wd"], eps=HYPER["eps"], a=HYPER["a"],
+              b=HYPER["b"], c=HYPER["c"])
+    groups = slice_shapes(ts)
+    per_shape = budget_s / len(groups)
+
+    def one(td, steps):
+        t1 = time.perf_counter()
+        oracle.muon_step(td.grad, td.momentum, td.master, steps=steps, **hp)
+        return time.perf_counter() - t1
+
+    parts, est_total, measured = [], 0.0, 0.0
+    for (shape, dtype), spec, count in groups:
+        td = make_tensor(wl, spec)
+        if len(spec.shape) == 3:        # the first slice of a 3-D tensor, as its own 2-D tensor
+            td.grad, td.momentum, td.master = (np.ascontiguousarray(a[0]) for a in
+                                               (td.grad, td.momentum, td.master))
+        f = ns_flops([type(spec)(spec.index, spec.name, shape, dtype)], k)
+        if f / est_rate <= per_shape:
+            tot, passes = 0.0, 0
+            while passes < max_passes and (passes == 0 or tot < min_s / len(groups)):
+                tot += one(td, k)
+                passes += 1
+            t_slice = tot / passes
+            measured += tot
+            how = f"{shape[0]}x{shape[1]}: full step x{passes}"
+        else:
+            t0 = one(td, 0)
+            t1 = one(td, 1)
+            measured += t0 + t1
+            t_slice = t0 + k * (t1 - t0)
+            how = (f"{shape[0]}x{shape[1]}: step at k=0 ({t0:.2f} s) and k=1 ({t1:.2f} s), "
+                   f"extrapolated to k={k}")
+        est_total += count * t_slice
+        parts.append(f"{how}, {t_slice:.3f} s per slice, x{count} slices")
+        del td
+    slices = sum(c for _, _, c in groups)
+    return {"value": slices / est_total, "unit": "matrices/s", "cores": int(blas_threads()),
+            "kind": "oracle",
+            "sample": "one 2-D slice of each distinct slice shape of the workload, fp64 numpy oracle; "
+                      + "; ".join(parts) + f"; step time = sum over shapes = {est_total:.1f} s; "
+                      f"{measured:.1f} s of oracle time measured",
+            "seconds_per_step": est_total, "seconds_measured": measured,
+            "gflops_fp64": ns_flops(ts, k) / est_total / 1e9}
 
 
 def adamw_bytes_per_elem(grad_dtype, publish):
@@ -191,12 +264,7 @@ def cpu_baseline_adamw(wl, budget_elems=1 << 24, min_s=10.0, max_passes=64):
     in passes over them until min_s of measured time (at most max_passes)."""
     import oracle
     from matrix_optimizer_muon_amd.workloads import make_adamw
-    try:
-        from threadpoolctl import threadpool_info
-        threads = max([p.get("num_threads", 1) for p in threadpool_info()
-                       if p.get("user_api") == "blas"] or [1])
-    except Exception:  # pragma: no cover
-        threads = os.cpu_count() or 1
+    threads = blas_threads()
     chosen, n_el = [], 0
     for t in wl.tensors:
         if chosen and n_el + t.shape[0] > budget_elems:
@@ -339,11 +407,9 @@ def main():
         del td
     stream = torch.cuda.current_stream()
 
-    def prepare():
-        need = mm.muon_step_workspace_size(grads, moms, masters, precision=args.precision)
-        ws = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
-        return mm.MuonStep(grads, moms, masters, precision=args.precision, workspace=ws,
-                           param_outs=pubs if args.publish else None)
+    def prepare(groups):
+        return mm.MuonStep(grads, moms, masters, precision=args.precision, stream_groups=groups,
+                           param_outs=pubs if args.publish else None, stream=stream)
 
     def timed(prepared, events):
         for _ in range(args.warmup):
@@ -362,21 +428,11 @@ def main():
         mm.phase_timing(False)
         return ev0.elapsed_time(ev1) / args.steps, wall, mm.phase_timing_read()
 
-    def with_groups(n, fn):
-        old = os.environ.get("DMUON_STREAM_GROUPS")
-        if n:
-            os.environ["DMUON_STREAM_GROUPS"] = str(n)
-        try:
-            return fn()
-        finally:
-            if n:
-                if old is None:
-                    del os.environ["DMUON_STREAM_GROUPS"]
-                else:
-                    os.environ["DMUON_STREAM_GROUPS"] = old
-
     # pass 1: throughput in the library's launch configuration
-    ms_step, wall, _ = with_groups(args.stream_groups, lambda: timed(prepare(), False))
+    first = prepare(args.stream_groups)
+    groups_used = first.groups
+    ms_step, wall, _ = timed(first, False)
+    del first
     slices = n_slices(ts)
     flops = ns_flops(ts, HYPER["steps"])
     tflops = flops / (ms_step * 1e-3) / 1e12
@@ -385,7 +441,7 @@ def main():
     roof, phases, ms_alone = None, {}, None
     pf = phase_flops(ts)
     if not args.no_phase_timing:
-        ms_alone, _, phases = with_groups(1, lambda: timed(prepare(), True))
+        ms_alone, _, phases = timed(prepare(1), True)
         dom = max(("gram", "square", "apply"), key=lambda p: phases[p][0])
         ms_tot, cnt = phases[dom]
         if cnt:
@@ -400,6 +456,22 @@ def main():
                     "launches": cnt,
                     "timing": "HIP events around each launch on its stream, one stream group, "
                               f"{args.steps} timed steps ({ms_alone:.4f} ms per step)"}
+
+    elementwise = None
+    if phases and phases.get("ingest", (0.0, 0))[1]:
+        ms_i, cnt_i = phases["ingest"]
+        elems = sum(int(np.prod(t.shape)) for t in ts)
+        alg, moved = ingest_bytes_per_elem(ts[0].grad_dtype, args.precision)
+        avg_i = ms_i / cnt_i
+        ach = elems * alg / (avg_i * 1e-3) / 1e9
+        ceil = copy_ceiling_gbs()
+        elementwise = {"kernel": "ingest", "bound": "hbm", "avg_launch_ms": round(avg_i, 4),
+                       "elements": elems, "bytes_per_elem": alg, "bytes_per_elem_moved": moved,
+                       "achieved": round(ach, 1), "achieved_moved": round(elems * moved / (avg_i * 1e-3) / 1e9, 1),
+                       "unit": "GB/s", "peak": PEAK_HBM_GBS, "frac": round(ach / PEAK_HBM_GBS, 4),
+                       "copy_ceiling": round(ceil, 1), "frac_of_copy": round(ach / ceil, 4),
+                       "target_frac": 0.8,
+                       "note": "the decay + update runs inside the last apply launch (no separate kernel)"}
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -420,11 +492,12 @@ def main():
         "tflops_effective": round(tflops, 2),
         "pct_bf16_peak": round(100 * tflops / PEAK_BF16_TFLOPS, 2),
         "config": {"workload": args.workload, "matrices": slices, "shapes": shapes,
-                   "stream_groups": args.stream_groups or "library",
+                   "stream_groups": groups_used,
                    "ns_steps": HYPER["steps"], "grad_dtype": ts[0].grad_dtype,
                    "effective_gflop_per_step": round(flops / 1e9, 1), "publish": bool(args.publish)},
         "roofline": roof,
         "cpu_baseline": cpu,
+        "elementwise": elementwise,
         "phases_ms_per_step": {k: round(v[0] / args.steps, 4) for k, v in phases.items() if v[1]},
         # one-stream pass: Newton–Schulz contractions alone, element-wise kernels alone
         "ns_ms_per_step": round(sum(phases[p][0] for p in ("gram", "square", "apply") if p in phases)

@@ -33,18 +33,22 @@
  * - `stream` is a hipStream_t passed as void* (NULL = the null stream).  Every
  *   GPU entry point only ENQUEUES work on `stream` and returns; the caller keeps
  *   every buffer alive until that work completes.
- * - The caller owns and frees all memory, including the workspace.  The library
- *   allocates no device memory.  Between calls it keeps only the opt-in
- *   phase-timing events (dmuon_phase_timing), eight pinned host buffers (with
- *   one event each) through which a call stages its tensor table to the
- *   workspace, so that the host need not wait for the stream, and, per device,
- *   the three streams (default priority) and four events with which a step
- *   split into concurrent groups forks from and joins back to `stream`.
+ * - The caller owns and frees all memory, including the workspace, and every
+ *   stream.  The library allocates no device or host memory that outlives a
+ *   call and keeps no streams or events between calls; the one exception is
+ *   the opt-in phase timing (dmuon_phase_timing), which holds its events until
+ *   they are read.
+ * - A call's tables (tensor descriptors, launch prefixes) are built on the host
+ *   and copied into the workspace by small kernels whose arguments carry them,
+ *   enqueued on `stream`; so every entry point may be captured into a HIP graph
+ *   (replays copy the same bytes and launch the same kernels).
  * - Every argument is validated on the host, before anything is enqueued, so a
  *   rejected call leaves all buffers untouched.  Validation makes no HIP call.
- * - The staged table copy reads a pinned buffer that later calls reuse, so it
- *   must not be replayed from a HIP graph: a call on a stream that is capturing
- *   a graph returns DMUON_E_HIP before enqueuing anything.
+ * - DMUON_TEST_FAIL_AT (environment, for failure-handling tests) makes a valid
+ *   call return DMUON_E_HIP at a named point as a failed HIP call would:
+ *   "plan" (before anything is enqueued), "table" (the table copy) or a phase
+ *   name ("ingest", "norm", "gram", "square", "apply", "update", "adamw": that
+ *   phase's first launch, the earlier launches being enqueued).
  * - Return value: DMUON_OK or a negative DMUON_E_* code; dmuon_last_error()
  *   then gives a message (thread-local, valid until the next call on the thread).
  * - After DMUON_E_HIP (a HIP launch/copy failed after validation) the contents
@@ -117,7 +121,8 @@ typedef struct {
  * to the Frobenius norm.  (a, b, c) are the page's (α, β, γ).  0 ≤ ns_steps ≤ 64.
  * prec is a dmuon_prec.  grad_scale (s, finite) multiplies the gradient as it is
  * read: 1 for an averaged reduce, 1/N for a summed one (HSDP guide, two-stage
- * gradient reduce: the net divisor is the number of contributing ranks). */
+ * gradient reduce: the net divisor is the number of contributing ranks).
+ * 0 ≤ stream_groups ≤ 4. */
 typedef struct {
   float lr;
   float momentum;
@@ -127,6 +132,10 @@ typedef struct {
   int32_t ns_steps;
   int32_t prec;
   float grad_scale;
+  int32_t stream_groups;    /* 0: the library's choice; 1..4: split the tensors
+                               into this many work-balanced groups (see
+                               dmuon_muon_step_run); the workspace layout
+                               depends on it */
 } dmuon_step_cfg;
 
 /* Bytes of workspace dmuon_muon_step needs for these tensors and cfg (host only,
@@ -134,15 +143,48 @@ typedef struct {
 int dmuon_muon_step_workspace_size(const dmuon_tensor* tensors, int32_t n_tensors,
                                    const dmuon_step_cfg* cfg, size_t* bytes);
 
+/* Number of work groups the step splits these tensors into (host only, no HIP
+ * call): cfg->stream_groups if set, else 4 when the workload is under four
+ * rounds of 256×256 output tiles on the 256 compute units (the groups' tail
+ * rounds then overlap each other's contractions), else 1; never more than the
+ * number of non-empty tensors. */
+int dmuon_muon_step_groups(const dmuon_tensor* tensors, int32_t n_tensors, const dmuon_step_cfg* cfg,
+                           int32_t* groups);
+
 /* The owner-rank Muon step over n_tensors tensors (all slices of all tensors in
- * one grouped launch per phase): momentum, per-slice normalisation, ns_steps
- * Newton–Schulz iterations, decoupled decay + lr-scaled update.
+ * one grouped launch per phase and group): momentum, per-slice normalisation,
+ * ns_steps Newton–Schulz iterations, decoupled decay + lr-scaled update.
  * DMuon architecture page §2 and §3.3 (owner-gated step); HSDP guide, "what
  * happens underneath", step 3.  n_tensors ≥ 0 (0 is a no-op); tensors may be
  * NULL only when n_tensors is 0.  The workspace (≥ the size reported above) is
- * scratch: its contents on entry are ignored and on exit are unspecified. */
+ * scratch apart from its table region: its contents on entry are ignored and
+ * on exit are unspecified.
+ *
+ * dmuon_muon_step = dmuon_muon_step_prepare followed by dmuon_muon_step_run.
+ * A caller that steps the same tensors repeatedly prepares once and runs each
+ * step: prepare writes the tables for exactly these tensor pointers, shapes,
+ * dtypes, cfg->prec and cfg->stream_groups into the workspace; run only
+ * launches the kernels, which read them.  The kernels of a run check a hash of
+ * the host-built table in every table entry they read: if the workspace does not
+ * hold the tables of a prepare with the same arguments (lr, momentum, weight
+ * decay, eps, a, b, c, ns_steps and grad_scale may differ), every workgroup
+ * exits at once and the run changes nothing.  The table region is written
+ * only by prepare, so runs may follow each other without a new prepare.
+ *
+ * Group 0 runs on `stream`; group g ≥ 1 runs on side_streams[(g − 1) mod
+ * n_side_streams], forked from `stream` and joined back to it with events
+ * created and destroyed inside the call (with n_side_streams = 0 every group
+ * runs on `stream`, in order).  The caller owns the side streams (non-NULL; use
+ * default-priority streams).  Results do not depend on the grouping or on the
+ * streams. */
 int dmuon_muon_step(const dmuon_tensor* tensors, int32_t n_tensors, const dmuon_step_cfg* cfg,
-                    void* workspace, size_t workspace_bytes, void* stream);
+                    void* workspace, size_t workspace_bytes, void* stream, void* const* side_streams,
+                    int32_t n_side_streams);
+int dmuon_muon_step_prepare(const dmuon_tensor* tensors, int32_t n_tensors, const dmuon_step_cfg* cfg,
+                            void* workspace, size_t workspace_bytes, void* stream);
+int dmuon_muon_step_run(const dmuon_tensor* tensors, int32_t n_tensors, const dmuon_step_cfg* cfg,
+                        void* workspace, size_t workspace_bytes, void* stream, void* const* side_streams,
+                        int32_t n_side_streams);
 
 /* Bytes of workspace dmuon_ns_batched needs (host only, no HIP call). */
 int dmuon_ns_batched_workspace_size(int64_t batch, int64_t rows, int64_t cols, int32_t prec,
@@ -256,7 +298,7 @@ int dmuon_phase_timing_read(double* ms, int64_t* count, int32_t n);
 const char* dmuon_last_error(void);
 
 /* ABI version (bumped on any change of a signature, a struct or a documented
- * numbering such as the phases above). */
+ * numbering such as the phases above): 4. */
 int32_t dmuon_abi_version(void);
 
 #ifdef __cplusplus

@@ -28,11 +28,12 @@ ERRORS = {
 F32, BF16 = 0, 1
 PREC = {"bf16": 0, "f32": 1}
 PHASES = ["ingest", "norm", "gram", "square", "apply", "update", "gemm_nt", "adamw"]
-EXPORTED = ["dmuon_muon_step_workspace_size", "dmuon_muon_step", "dmuon_ns_batched_workspace_size",
+EXPORTED = ["dmuon_muon_step_workspace_size", "dmuon_muon_step_groups", "dmuon_muon_step",
+            "dmuon_muon_step_prepare", "dmuon_muon_step_run", "dmuon_ns_batched_workspace_size",
             "dmuon_ns_batched", "dmuon_lpt_assign", "dmuon_adamw_step_workspace_size",
             "dmuon_adamw_step", "dmuon_gemm_nt", "dmuon_phase_timing", "dmuon_phase_timing_read",
             "dmuon_last_error", "dmuon_abi_version"]
-ABI_VERSION = 3
+ABI_VERSION = 4
 
 
 class DmuonError(Exception):
@@ -51,7 +52,7 @@ class StepCfg(ctypes.Structure):
                 ("weight_decay", ctypes.c_float), ("eps", ctypes.c_float),
                 ("a", ctypes.c_float), ("b", ctypes.c_float), ("c", ctypes.c_float),
                 ("ns_steps", ctypes.c_int32), ("prec", ctypes.c_int32),
-                ("grad_scale", ctypes.c_float)]
+                ("grad_scale", ctypes.c_float), ("stream_groups", ctypes.c_int32)]
 
 
 class AdamwTensor(ctypes.Structure):
@@ -82,7 +83,10 @@ def lib():
                              ctypes.c_size_t)
     P = ctypes.POINTER
     L.dmuon_muon_step_workspace_size.argtypes = [P(Tensor), i32, P(StepCfg), P(sz)]
-    L.dmuon_muon_step.argtypes = [P(Tensor), i32, P(StepCfg), vp, sz, vp]
+    L.dmuon_muon_step_groups.argtypes = [P(Tensor), i32, P(StepCfg), P(i32)]
+    L.dmuon_muon_step.argtypes = [P(Tensor), i32, P(StepCfg), vp, sz, vp, P(vp), i32]
+    L.dmuon_muon_step_prepare.argtypes = [P(Tensor), i32, P(StepCfg), vp, sz, vp]
+    L.dmuon_muon_step_run.argtypes = [P(Tensor), i32, P(StepCfg), vp, sz, vp, P(vp), i32]
     L.dmuon_ns_batched_workspace_size.argtypes = [i64, i64, i64, i32, i32, P(sz)]
     L.dmuon_ns_batched.argtypes = [vp, i32, vp, i64, i64, i64, f32, f32, f32, i32, f32, i32, i32,
                                    vp, sz, vp]
@@ -95,7 +99,8 @@ def lib():
     L.dmuon_last_error.restype = ctypes.c_char_p
     L.dmuon_last_error.argtypes = []
     L.dmuon_abi_version.restype = i32
-    for name in ["dmuon_muon_step_workspace_size", "dmuon_muon_step",
+    for name in ["dmuon_muon_step_workspace_size", "dmuon_muon_step_groups", "dmuon_muon_step",
+                 "dmuon_muon_step_prepare", "dmuon_muon_step_run",
                  "dmuon_ns_batched_workspace_size", "dmuon_ns_batched", "dmuon_lpt_assign",
                  "dmuon_adamw_step_workspace_size", "dmuon_adamw_step",
                  "dmuon_gemm_nt", "dmuon_phase_timing", "dmuon_phase_timing_read"]:
@@ -124,11 +129,32 @@ def _torch():
     return torch
 
 
-def _stream_handle(stream):
+def resolve_stream(stream):
+    """The torch stream a call runs on (the current stream when None)."""
     torch = _torch()
-    if stream is None:
-        stream = torch.cuda.current_stream()
-    return ctypes.c_void_p(stream.cuda_stream)
+    return torch.cuda.current_stream() if stream is None else stream
+
+
+def _stream_handle(stream):
+    return ctypes.c_void_p(resolve_stream(stream).cuda_stream)
+
+
+def stream_array(streams):
+    """ctypes array of hipStream_t handles (and its length)."""
+    arr = (ctypes.c_void_p * max(len(streams), 1))(*[s.cuda_stream for s in streams])
+    return arr, len(streams)
+
+
+def keep_until_done(tensor, streams):
+    """Tell torch's caching allocator that ``tensor`` is used on ``streams``, so
+    that its block is not handed out again before their queued work completes
+    (it only tracks the stream the block was allocated on).  Skipped during
+    graph capture, where the graph keeps its memory."""
+    torch = _torch()
+    if tensor is None or torch.cuda.is_current_stream_capturing():
+        return
+    for st in streams:
+        tensor.record_stream(st)
 
 
 def _dtype_code(t):
@@ -152,11 +178,13 @@ def _check_dev(t, what, dtype=None):
         raise ValueError(f"{what} must be {dtype}, got {t.dtype}")
 
 
-def make_cfg(lr, momentum, weight_decay, eps, coeffs, steps, precision, grad_scale=1.0) -> StepCfg:
+def make_cfg(lr, momentum, weight_decay, eps, coeffs, steps, precision, grad_scale=1.0,
+             stream_groups=0) -> StepCfg:
     if precision not in PREC:
         raise ValueError(f"precision must be one of {sorted(PREC)}")
     a, b, c = coeffs
-    return StepCfg(lr, momentum, weight_decay, eps, a, b, c, int(steps), PREC[precision], grad_scale)
+    return StepCfg(lr, momentum, weight_decay, eps, a, b, c, int(steps), PREC[precision], grad_scale,
+                   int(stream_groups))
 
 
 def _bf16_words(t, what, shape):
@@ -241,9 +269,19 @@ def muon_step_workspace_size(cfg: StepCfg, descs) -> int:
     return out.value
 
 
-def alloc_workspace(nbytes, device):
+def muon_step_groups(cfg: StepCfg, descs) -> int:
+    arr, n = descs
+    out = ctypes.c_int32(0)
+    check(lib().dmuon_muon_step_groups(arr, n, ctypes.byref(cfg), ctypes.byref(out)))
+    return out.value
+
+
+def alloc_workspace(nbytes, device, stream=None):
+    """uint8 device buffer of ``nbytes`` allocated on ``stream`` (the stream its
+    kernels run on, so the allocator orders its reuse after them)."""
     torch = _torch()
-    return torch.empty(max(int(nbytes), 1), dtype=torch.uint8, device=device)
+    with torch.cuda.stream(resolve_stream(stream)):
+        return torch.empty(max(int(nbytes), 1), dtype=torch.uint8, device=device)
 
 
 def lpt_assign_np(rows, cols, batch, layer_id, n_slots, merge_below_elems=0, cost_kind=0,

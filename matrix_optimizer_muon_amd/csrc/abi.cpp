@@ -75,43 +75,57 @@ void timing_after(int phase, void* stream) {
 }
 
 // ---------------------------------------------------------------------------
-// table upload through pinned staging
+// tables
 //
-// The per-call tensor table is copied host → device on the caller's stream.  A
-// copy from pageable memory may hold the host until the stream reaches it, so
-// the host could not enqueue ahead of the GPU.  The table is staged instead in
-// one of kStaging pinned buffers; an event recorded after each copy tells when
-// the buffer may be reused (by then it is long done: kStaging calls later).
+// A call's tables (problem descriptors and per-phase workgroup prefixes) are
+// built on the host and carried into the workspace in the kernel arguments of
+// small copy kernels on the caller's stream (launch_write_table), so the
+// library keeps no host staging memory, no host buffer has to outlive the
+// call, and a captured graph replays the same bytes.  Every problem entry
+// carries a tag, the FNV-1a hash of the whole host table; the step's kernels
+// are launched with the tag they expect, and a workgroup that finds another
+// one exits before touching memory, so a launch on a workspace that does not
+// hold its plan's table does nothing.
 // ---------------------------------------------------------------------------
-constexpr int kStaging = 8;
-struct Staging {
-  void* host = nullptr;
-  size_t cap = 0;
-  hipEvent_t done = nullptr;
-};
-static std::mutex g_smu;
-static Staging g_stage[kStaging];
-static int g_stage_next = 0;
-
-static int stage_upload(void* dst, const void* src, size_t bytes, void* stream) {
-  std::lock_guard<std::mutex> lk(g_smu);
-  Staging& st = g_stage[g_stage_next];
-  g_stage_next = (g_stage_next + 1) % kStaging;
-  hipError_t e;
-  if (st.done && (e = hipEventSynchronize(st.done)) != hipSuccess) return (int)e;
-  if (st.cap < bytes) {
-    if (st.host && (e = hipHostFree(st.host)) != hipSuccess) return (int)e;
-    st.host = nullptr;
-    st.cap = 0;
-    const size_t cap = std::max<size_t>(bytes, 64 << 10);
-    if ((e = hipHostMalloc(&st.host, cap, hipHostMallocDefault)) != hipSuccess) return (int)e;
-    st.cap = cap;
+static uint32_t fnv1a(const char* p, size_t n) {
+  uint32_t h = 2166136261u;
+  for (size_t i = 0; i < n; ++i) {
+    h ^= (uint8_t)p[i];
+    h *= 16777619u;
   }
-  std::memcpy(st.host, src, bytes);
-  if ((e = hipMemcpyAsync(dst, st.host, bytes, hipMemcpyHostToDevice, (hipStream_t)stream)) != hipSuccess)
-    return (int)e;
-  if (!st.done && (e = hipEventCreateWithFlags(&st.done, hipEventDisableTiming)) != hipSuccess) return (int)e;
-  return (int)hipEventRecord(st.done, (hipStream_t)stream);
+  return h;
+}
+
+// Forced failures for the failure-handling tests: DMUON_TEST_FAIL_AT names the
+// point at which a valid call returns DMUON_E_HIP as a failed HIP call would:
+// "plan" (after validation, before anything is enqueued), "table" (the table
+// copy), or a phase name (that phase's first launch; earlier launches are
+// enqueued).
+struct FailAt {
+  int where = -3;   // -3 none, -2 plan, -1 table, else a phase id
+};
+static FailAt fail_at() {
+  FailAt f;
+  const char* v = std::getenv("DMUON_TEST_FAIL_AT");
+  if (!v) return f;
+  static const char* names[PH_COUNT] = {"ingest", "norm", "gram", "square", "apply", "update", "gemm_nt", "adamw"};
+  if (std::strcmp(v, "plan") == 0) f.where = -2;
+  else if (std::strcmp(v, "table") == 0) f.where = -1;
+  for (int i = 0; i < PH_COUNT; ++i)
+    if (std::strcmp(v, names[i]) == 0) f.where = i;
+  return f;
+}
+static int forced(const FailAt& f, int where) {
+  if (f.where != where) return DMUON_OK;
+  return fail(DMUON_E_HIP, std::string("forced failure (DMUON_TEST_FAIL_AT=") + std::getenv("DMUON_TEST_FAIL_AT") + ")");
+}
+
+static int write_table(void* dst, const std::vector<char>& host, void* stream, const FailAt& fa) {
+  int e = forced(fa, -1);
+  if (e) return e;
+  e = launch_write_table(dst, host.data(), host.size(), stream);
+  if (e) return fail(DMUON_E_HIP, std::string("table copy: ") + hip_error_string(e));
+  return DMUON_OK;
 }
 
 // ---------------------------------------------------------------------------
@@ -133,7 +147,23 @@ struct Plan {
   int64_t total_slices = 0;
   int64_t total_wg[PH_COUNT] = {};
   size_t off_prefix = 0, off_scal = 0, table_bytes = 0, bytes = 0;
+  uint32_t tag = 0;
 };
+
+// The device image of the plan's tables, with every entry's tag set.
+static std::vector<char> seal(Plan& pl) {
+  std::vector<char> host(pl.table_bytes, 0);
+  for (DevProblem& P : pl.probs) P.tag = 0;
+  auto fill = [&] {
+    std::memcpy(host.data(), pl.probs.data(), pl.probs.size() * sizeof(DevProblem));
+    std::memcpy(host.data() + pl.off_prefix, pl.prefix.data(), pl.prefix.size() * sizeof(int32_t));
+  };
+  fill();
+  pl.tag = fnv1a(host.data(), host.size());
+  for (DevProblem& P : pl.probs) P.tag = pl.tag;
+  fill();
+  return host;
+}
 
 static size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
@@ -234,24 +264,24 @@ static int build_plan(const std::vector<Item>& items, int prec_f32, Plan& pl, ch
   return DMUON_OK;
 }
 
-static int run_plan(Plan& pl, char* ws, int prec_f32, const LaunchScalars& base_s, int steps, void* stream) {
-  // descriptors + prefix arrays: one host → device copy, ordered on the stream
-  std::vector<char> host(pl.table_bytes, 0);
-  std::memcpy(host.data(), pl.probs.data(), pl.probs.size() * sizeof(DevProblem));
-  std::memcpy(host.data() + pl.off_prefix, pl.prefix.data(), pl.prefix.size() * sizeof(int32_t));
-  int e = stage_upload(ws, host.data(), host.size(), stream);
-  if (e) return fail(DMUON_E_HIP, std::string("table upload: ") + hip_error_string(e));
+// Enqueue the phases of one plan whose tables are in the workspace at ws.
+static int launch_plan(const Plan& pl, char* ws, int prec_f32, const LaunchScalars& base_s, int steps,
+                       void* stream, const FailAt& fa) {
   LaunchTable tab;
   tab.probs = (const DevProblem*)ws;
   tab.wg_prefix = (const int32_t*)(ws + pl.off_prefix);
   tab.scal = (float*)(ws + pl.off_scal);
   tab.n_probs = (int32_t)pl.probs.size();
+  tab.tag = pl.tag;
   auto go = [&](int ph, const LaunchScalars& s) -> int {
+    int e = forced(fa, ph);
+    if (e) return e;
     tab.total_wg = (int32_t)pl.total_wg[ph];
     const int r = launch_phase(ph, prec_f32, tab, s, stream);
     if (r) return fail(DMUON_E_HIP, std::string("launch failed: ") + hip_error_string(r));
     return DMUON_OK;
   };
+  int e;
   LaunchScalars s = base_s;
   s.t = 0;
   s.last = 0;
@@ -293,14 +323,11 @@ constexpr int kMaxGroups = 4;
 //   experts: 116.1 / 122.0; 384 small matrices: 2.74 / 2.76).
 constexpr int kCusAssumed = 256;
 
-static int group_count(const std::vector<Item>& items) {
+// requested: the cfg's stream_groups (0: the rule above).
+static int group_count(const std::vector<Item>& items, int requested) {
   double tiles = 0;
   for (const Item& it : items) tiles += (double)it.batch * cdiv(it.rows, kTile) * cdiv(it.cols, kTile);
-  int g = tiles < 4.0 * kCusAssumed ? 4 : 1;
-  if (const char* v = std::getenv("DMUON_STREAM_GROUPS")) {   // tuning override, 1..4
-    const int x = std::atoi(v);
-    if (x >= 1 && x <= kMaxGroups) g = x;
-  }
+  const int g = requested >= 1 ? requested : (tiles < 4.0 * kCusAssumed ? 4 : 1);
   return std::min<int>(g, (int)items.size());
 }
 
@@ -318,9 +345,9 @@ struct GroupPlan {
   size_t bytes = 0;
 };
 
-// Split the items, size (base == nullptr) or lay out every group's plan.
-static int plan_groups(const std::vector<Item>& items, int prec_f32, char* base, GroupPlan& gp) {
-  const int G = group_count(items);
+// Split the items into G groups, size (base == nullptr) or lay out every group's plan.
+static int plan_groups(const std::vector<Item>& items, int prec_f32, int requested, char* base, GroupPlan& gp) {
+  const int G = group_count(items, requested);
   std::vector<std::vector<Item>> groups(G);
   std::vector<int> order(items.size());
   for (size_t i = 0; i < items.size(); ++i) order[i] = (int)i;
@@ -348,56 +375,49 @@ static int plan_groups(const std::vector<Item>& items, int prec_f32, char* base,
   return DMUON_OK;
 }
 
-struct DeviceStreams {
-  hipStream_t s[kMaxGroups - 1] = {};
-  hipEvent_t fork = nullptr;
-  hipEvent_t join[kMaxGroups - 1] = {};
-  std::mutex mu;
-};
-static std::mutex g_dsmu;
-static std::vector<DeviceStreams*> g_ds;
-
-// Library streams and events of the current device (created on first use, kept
-// until the process ends; default priority).
-static int device_streams(DeviceStreams** out) {
-  int dev = 0;
-  hipError_t e = hipGetDevice(&dev);
-  if (e != hipSuccess) return (int)e;
-  std::lock_guard<std::mutex> lk(g_dsmu);
-  if ((int)g_ds.size() <= dev) g_ds.resize(dev + 1, nullptr);
-  if (!g_ds[dev]) {
-    DeviceStreams* d = new DeviceStreams();
-    for (int i = 0; i < kMaxGroups - 1; ++i) {
-      if ((e = hipStreamCreateWithFlags(&d->s[i], hipStreamNonBlocking)) != hipSuccess) return (int)e;
-      if ((e = hipEventCreateWithFlags(&d->join[i], hipEventDisableTiming)) != hipSuccess) return (int)e;
-    }
-    if ((e = hipEventCreateWithFlags(&d->fork, hipEventDisableTiming)) != hipSuccess) return (int)e;
-    g_ds[dev] = d;
+// Copy every group's tables into the workspace, on the caller's stream.
+static int write_groups(GroupPlan& gp, char* ws, void* stream, const FailAt& fa) {
+  for (size_t g = 0; g < gp.plans.size(); ++g) {
+    const std::vector<char> host = seal(gp.plans[g]);
+    const int e = write_table(ws + gp.offs[g], host, stream, fa);
+    if (e) return e;
   }
-  *out = g_ds[dev];
-  return 0;
+  return DMUON_OK;
 }
 
-static int run_groups(GroupPlan& gp, char* ws, int prec_f32, const LaunchScalars& s, int steps, void* stream) {
+// Enqueue every group's phases.  Group 0 runs on `stream`, group g ≥ 1 on
+// side[(g − 1) % n_side] (on `stream` too when n_side is 0).  The side streams
+// fork from `stream` and join back to it through events made for this call and
+// released before it returns (HIP keeps a recorded event's pending work alive).
+static int launch_groups(GroupPlan& gp, char* ws, int prec_f32, const LaunchScalars& s, int steps, void* stream,
+                         void* const* side, int n_side, const FailAt& fa) {
   const int G = (int)gp.plans.size();
-  if (G == 1) return run_plan(gp.plans[0], ws + gp.offs[0], prec_f32, s, steps, stream);
-  DeviceStreams* d = nullptr;
-  int r = device_streams(&d);
-  if (r) return fail(DMUON_E_HIP, std::string("stream setup: ") + hip_error_string(r));
-  std::lock_guard<std::mutex> lk(d->mu);
+  for (Plan& pl : gp.plans) (void)seal(pl);       // the tags the kernels expect
+  const int used = n_side > 0 ? std::min(G - 1, n_side) : 0;
   hipStream_t caller = (hipStream_t)stream;
-  if ((r = (int)hipEventRecord(d->fork, caller)) != 0) return fail(DMUON_E_HIP, std::string("fork: ") + hip_error_string(r));
-  for (int g = 1; g < G; ++g)
-    if ((r = (int)hipStreamWaitEvent(d->s[g - 1], d->fork, 0)) != 0)
-      return fail(DMUON_E_HIP, std::string("fork wait: ") + hip_error_string(r));
+  int r;
+  if (used > 0) {
+    hipEvent_t fork = nullptr;
+    if ((r = (int)hipEventCreateWithFlags(&fork, hipEventDisableTiming)) != 0)
+      return fail(DMUON_E_HIP, std::string("fork event: ") + hip_error_string(r));
+    r = (int)hipEventRecord(fork, caller);
+    for (int i = 0; i < used && r == 0; ++i) r = (int)hipStreamWaitEvent((hipStream_t)side[i], fork, 0);
+    (void)hipEventDestroy(fork);
+    if (r) return fail(DMUON_E_HIP, std::string("fork: ") + hip_error_string(r));
+  }
   int rc = DMUON_OK;
-  for (int g = 0; g < G && rc == DMUON_OK; ++g)
-    rc = run_plan(gp.plans[g], ws + gp.offs[g], prec_f32, s, steps, g == 0 ? stream : (void*)d->s[g - 1]);
-  // join every library stream back, also after a failed launch
-  for (int g = 1; g < G; ++g) {
-    if ((r = (int)hipEventRecord(d->join[g - 1], d->s[g - 1])) != 0 ||
-        (r = (int)hipStreamWaitEvent(caller, d->join[g - 1], 0)) != 0)
-      if (rc == DMUON_OK) rc = fail(DMUON_E_HIP, std::string("join: ") + hip_error_string(r));
+  for (int g = 0; g < G && rc == DMUON_OK; ++g) {
+    void* st = (g == 0 || used == 0) ? stream : side[(g - 1) % used];
+    rc = launch_plan(gp.plans[g], ws + gp.offs[g], prec_f32, s, steps, st, fa);
+  }
+  // join every side stream back, also after a failed launch
+  for (int i = 0; i < used; ++i) {
+    hipEvent_t join = nullptr;
+    r = (int)hipEventCreateWithFlags(&join, hipEventDisableTiming);
+    if (r == 0) r = (int)hipEventRecord(join, (hipStream_t)side[i]);
+    if (r == 0) r = (int)hipStreamWaitEvent(caller, join, 0);
+    if (join) (void)hipEventDestroy(join);
+    if (r && rc == DMUON_OK) rc = fail(DMUON_E_HIP, std::string("join: ") + hip_error_string(r));
   }
   return rc;
 }
@@ -438,6 +458,8 @@ static int check_cfg(const dmuon_step_cfg* cfg) {
   if (!finite(cfg->lr) || !finite(cfg->momentum) || !finite(cfg->weight_decay) || !finite(cfg->a) ||
       !finite(cfg->b) || !finite(cfg->c) || !finite(cfg->grad_scale))
     return fail(DMUON_E_CFG, "hyper-parameters must be finite");
+  if (cfg->stream_groups < 0 || cfg->stream_groups > kMaxGroups)
+    return fail(DMUON_E_CFG, "stream_groups must be in [0, 4], got " + std::to_string(cfg->stream_groups));
   return DMUON_OK;
 }
 
@@ -484,24 +506,48 @@ static int check_workspace(void* ws, size_t have, size_t need) {
   return DMUON_OK;
 }
 
-// The table copy reads a pinned staging buffer that later calls reuse: captured
-// into a graph, its replays would read whatever that buffer then holds.
-static int refuse_capture(void* stream) {
-  hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
-  const hipError_t e = hipStreamIsCapturing((hipStream_t)stream, &cs);
-  if (e != hipSuccess) return fail(DMUON_E_HIP, std::string("stream query: ") + hip_error_string((int)e));
-  if (cs != hipStreamCaptureStatusNone)
-    return fail(DMUON_E_HIP, "the stream is capturing a graph: the step stages its tables through a reused "
-                             "host buffer and cannot be captured");
+static int check_side(void* const* side, int32_t n_side) {
+  if (n_side < 0) return fail(DMUON_E_CFG, "n_side_streams < 0");
+  if (n_side > 0 && !side) return fail(DMUON_E_NULL, "side_streams is NULL");
+  for (int32_t i = 0; i < n_side; ++i)
+    if (!side[i]) return fail(DMUON_E_NULL, "side_streams[" + std::to_string(i) + "] is NULL (the null stream)");
   return DMUON_OK;
 }
 
-static int test_fail_hook() {
-  // DMUON_TEST_FAIL_AT=plan makes a valid call fail as a HIP error would, before
-  // anything is enqueued (used by the host-side failure tests).
-  const char* v = std::getenv("DMUON_TEST_FAIL_AT");
-  if (v && std::strcmp(v, "plan") == 0) return fail(DMUON_E_HIP, "forced failure (DMUON_TEST_FAIL_AT=plan)");
-  return DMUON_OK;
+// Validation shared by the step entry points: cfg, tensors, overlaps, the
+// workspace; on success `gp` holds the plan laid out on the workspace.
+static int prepare_step(const dmuon_tensor* tensors, int32_t n, const dmuon_step_cfg* cfg, void* workspace,
+                        size_t workspace_bytes, std::vector<Item>& items, GroupPlan& gp) {
+  int e = check_cfg(cfg);
+  if (e) return e;
+  std::vector<Range> rs;
+  if ((e = collect_items(tensors, n, items, &rs))) return e;
+  if (items.empty()) return DMUON_OK;
+  if ((e = check_alias(rs))) return e;
+  const int f32 = cfg->prec == DMUON_PREC_F32;
+  GroupPlan sized;
+  if ((e = plan_groups(items, f32, cfg->stream_groups, nullptr, sized))) return e;
+  if ((e = check_workspace(workspace, workspace_bytes, sized.bytes))) return e;
+  const uintptr_t wlo = (uintptr_t)workspace, whi = wlo + sized.bytes;
+  for (const Range& r : rs)
+    if (r.lo < whi && wlo < r.hi) return fail(DMUON_E_ALIAS, "workspace overlaps a tensor buffer");
+  return plan_groups(items, f32, cfg->stream_groups, (char*)workspace, gp);
+}
+
+static LaunchScalars step_scalars(const dmuon_step_cfg* cfg) {
+  LaunchScalars s{};
+  s.mu = cfg->momentum;
+  s.lr = cfg->lr;
+  s.decay = (float)(1.0 - (double)cfg->lr * (double)cfg->weight_decay);
+  s.eps = cfg->eps;
+  s.a = cfg->a;
+  s.b = cfg->b;
+  s.c = cfg->c;
+  s.has_momentum = 1;
+  s.normalize = 1;
+  s.write_master = 1;
+  s.gscale = cfg->grad_scale;
+  return s;
 }
 
 // ---- the adamw route ------------------------------------------------------
@@ -510,7 +556,22 @@ struct AdamwPlan {
   std::vector<int32_t> prefix;      // n + 1
   int64_t total_wg = 0;
   size_t off_prefix = 0, bytes = 0;
+  uint32_t tag = 0;
 };
+
+static std::vector<char> seal(AdamwPlan& pl) {
+  std::vector<char> host(pl.bytes, 0);
+  for (AdamwProblem& P : pl.probs) P.tag = 0;
+  auto fill = [&] {
+    std::memcpy(host.data(), pl.probs.data(), pl.probs.size() * sizeof(AdamwProblem));
+    std::memcpy(host.data() + pl.off_prefix, pl.prefix.data(), pl.prefix.size() * sizeof(int32_t));
+  };
+  fill();
+  pl.tag = fnv1a(host.data(), host.size());
+  for (AdamwProblem& P : pl.probs) P.tag = pl.tag;
+  fill();
+  return host;
+}
 
 static int check_adamw_cfg(const dmuon_adamw_cfg* cfg) {
   if (!cfg) return fail(DMUON_E_NULL, "cfg is NULL");
@@ -588,7 +649,7 @@ using namespace dmuon;
 
 extern "C" {
 
-int32_t dmuon_abi_version(void) { return 3; }
+int32_t dmuon_abi_version(void) { return 4; }
 
 const char* dmuon_last_error(void) { return g_err.c_str(); }
 
@@ -605,45 +666,61 @@ int dmuon_muon_step_workspace_size(const dmuon_tensor* tensors, int32_t n, const
     return DMUON_OK;
   }
   GroupPlan gp;
-  if ((e = plan_groups(items, cfg->prec == DMUON_PREC_F32, nullptr, gp))) return e;
+  if ((e = plan_groups(items, cfg->prec == DMUON_PREC_F32, cfg->stream_groups, nullptr, gp))) return e;
   *bytes = gp.bytes;
   return DMUON_OK;
 }
 
-int dmuon_muon_step(const dmuon_tensor* tensors, int32_t n, const dmuon_step_cfg* cfg, void* workspace,
-                    size_t workspace_bytes, void* stream) {
+int dmuon_muon_step_groups(const dmuon_tensor* tensors, int32_t n, const dmuon_step_cfg* cfg, int32_t* groups) {
   g_err.clear();
+  if (!groups) return fail(DMUON_E_NULL, "groups is NULL");
   int e = check_cfg(cfg);
   if (e) return e;
   std::vector<Item> items;
-  std::vector<Range> rs;
-  if ((e = collect_items(tensors, n, items, &rs))) return e;
-  if (items.empty()) return DMUON_OK;
-  if ((e = check_alias(rs))) return e;
-  const int f32 = cfg->prec == DMUON_PREC_F32;
+  if ((e = collect_items(tensors, n, items, nullptr))) return e;
+  *groups = items.empty() ? 0 : group_count(items, cfg->stream_groups);
+  return DMUON_OK;
+}
+
+int dmuon_muon_step_prepare(const dmuon_tensor* tensors, int32_t n, const dmuon_step_cfg* cfg, void* workspace,
+                            size_t workspace_bytes, void* stream) {
+  g_err.clear();
+  std::vector<Item> items;
   GroupPlan gp;
-  if ((e = plan_groups(items, f32, nullptr, gp))) return e;
-  if ((e = check_workspace(workspace, workspace_bytes, gp.bytes))) return e;
-  const uintptr_t wlo = (uintptr_t)workspace, whi = wlo + gp.bytes;
-  for (const Range& r : rs)
-    if (r.lo < whi && wlo < r.hi) return fail(DMUON_E_ALIAS, "workspace overlaps a tensor buffer");
-  if ((e = test_fail_hook())) return e;
-  if ((e = refuse_capture(stream))) return e;
-  GroupPlan real;
-  if ((e = plan_groups(items, f32, (char*)workspace, real))) return e;
-  LaunchScalars s{};
-  s.mu = cfg->momentum;
-  s.lr = cfg->lr;
-  s.decay = (float)(1.0 - (double)cfg->lr * (double)cfg->weight_decay);
-  s.eps = cfg->eps;
-  s.a = cfg->a;
-  s.b = cfg->b;
-  s.c = cfg->c;
-  s.has_momentum = 1;
-  s.normalize = 1;
-  s.write_master = 1;
-  s.gscale = cfg->grad_scale;
-  return run_groups(real, (char*)workspace, f32, s, cfg->ns_steps, stream);
+  int e = prepare_step(tensors, n, cfg, workspace, workspace_bytes, items, gp);
+  if (e || items.empty()) return e;
+  const FailAt fa = fail_at();
+  if ((e = forced(fa, -2))) return e;
+  return write_groups(gp, (char*)workspace, stream, fa);
+}
+
+int dmuon_muon_step_run(const dmuon_tensor* tensors, int32_t n, const dmuon_step_cfg* cfg, void* workspace,
+                        size_t workspace_bytes, void* stream, void* const* side_streams, int32_t n_side_streams) {
+  g_err.clear();
+  int e = check_side(side_streams, n_side_streams);
+  if (e) return e;
+  std::vector<Item> items;
+  GroupPlan gp;
+  if ((e = prepare_step(tensors, n, cfg, workspace, workspace_bytes, items, gp)) || items.empty()) return e;
+  const FailAt fa = fail_at();
+  if ((e = forced(fa, -2))) return e;
+  return launch_groups(gp, (char*)workspace, cfg->prec == DMUON_PREC_F32, step_scalars(cfg), cfg->ns_steps,
+                       stream, side_streams, n_side_streams, fa);
+}
+
+int dmuon_muon_step(const dmuon_tensor* tensors, int32_t n, const dmuon_step_cfg* cfg, void* workspace,
+                    size_t workspace_bytes, void* stream, void* const* side_streams, int32_t n_side_streams) {
+  g_err.clear();
+  int e = check_side(side_streams, n_side_streams);
+  if (e) return e;
+  std::vector<Item> items;
+  GroupPlan gp;
+  if ((e = prepare_step(tensors, n, cfg, workspace, workspace_bytes, items, gp)) || items.empty()) return e;
+  const FailAt fa = fail_at();
+  if ((e = forced(fa, -2))) return e;
+  if ((e = write_groups(gp, (char*)workspace, stream, fa))) return e;
+  return launch_groups(gp, (char*)workspace, cfg->prec == DMUON_PREC_F32, step_scalars(cfg), cfg->ns_steps,
+                       stream, side_streams, n_side_streams, fa);
 }
 
 int dmuon_ns_batched_workspace_size(int64_t batch, int64_t rows, int64_t cols, int32_t prec, int32_t steps,
@@ -694,10 +771,11 @@ int dmuon_ns_batched(const void* x, int32_t x_dtype, float* out, int64_t batch, 
   const uintptr_t wlo = (uintptr_t)workspace, whi = wlo + pl.bytes;
   for (const Range& r : rs)
     if (r.lo < whi && wlo < r.hi) return fail(DMUON_E_ALIAS, "workspace overlaps x or out");
-  if ((e = test_fail_hook())) return e;
-  if ((e = refuse_capture(stream))) return e;
+  const FailAt fa = fail_at();
+  if ((e = forced(fa, -2))) return e;
   Plan real;
   if ((e = build_plan(items, f32, real, (char*)workspace))) return e;
+  if ((e = write_table(workspace, seal(real), stream, fa))) return e;
   LaunchScalars s{};
   s.eps = eps;
   s.a = a;
@@ -707,7 +785,7 @@ int dmuon_ns_batched(const void* x, int32_t x_dtype, float* out, int64_t batch, 
   s.normalize = normalize;
   s.write_master = 0;
   s.gscale = 1.f;
-  return run_plan(real, (char*)workspace, f32, s, steps, stream);
+  return launch_plan(real, (char*)workspace, f32, s, steps, stream, fa);
 }
 
 int dmuon_adamw_step_workspace_size(const dmuon_adamw_tensor* tensors, int32_t n, size_t* bytes) {
@@ -738,14 +816,10 @@ int dmuon_adamw_step(const dmuon_adamw_tensor* tensors, int32_t n, const dmuon_a
   const uintptr_t wlo = (uintptr_t)workspace, whi = wlo + pl.bytes;
   for (const Range& r : rs)
     if (r.lo < whi && wlo < r.hi) return fail(DMUON_E_ALIAS, "workspace overlaps a tensor buffer");
-  if ((e = test_fail_hook())) return e;
-  if ((e = refuse_capture(stream))) return e;
-  std::vector<char> host(pl.bytes, 0);
-  std::memcpy(host.data(), pl.probs.data(), pl.probs.size() * sizeof(AdamwProblem));
-  std::memcpy(host.data() + pl.off_prefix, pl.prefix.data(), pl.prefix.size() * sizeof(int32_t));
+  const FailAt fa = fail_at();
+  if ((e = forced(fa, -2))) return e;
   char* ws = (char*)workspace;
-  e = stage_upload(ws, host.data(), host.size(), stream);
-  if (e) return fail(DMUON_E_HIP, std::string("table upload: ") + hip_error_string(e));
+  if ((e = write_table(ws, seal(pl), stream, fa))) return e;
   // bias corrections in double on the host (step is exact as an integer)
   const double b1 = cfg->beta1, b2 = cfg->beta2;
   const double bc1 = 1.0 - std::pow(b1, (double)cfg->step);
@@ -765,6 +839,8 @@ int dmuon_adamw_step(const dmuon_adamw_tensor* tensors, int32_t n, const dmuon_a
   tab.wg_prefix = (const int32_t*)(ws + pl.off_prefix);
   tab.n_probs = (int32_t)pl.probs.size();
   tab.total_wg = (int32_t)pl.total_wg;
+  tab.tag = pl.tag;
+  if ((e = forced(fa, PH_ADAMW))) return e;
   const int r = launch_adamw(tab, s, stream);
   if (r) return fail(DMUON_E_HIP, std::string("launch failed: ") + hip_error_string(r));
   return DMUON_OK;

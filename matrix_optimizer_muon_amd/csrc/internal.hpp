@@ -33,6 +33,7 @@ enum Phase : int {
 // All per-slice arrays are laid out slice after slice with the given strides
 // (in elements of the array's type).
 struct DevProblem {
+  uint32_t tag;                // plan tag (see LaunchTable::tag)
   int32_t batch, rows, cols;   // storage shape of one slice (row-major)
   int32_t m, n;                // m = min(rows, cols), n = max
   int32_t wide;                // 1: rows <= cols (Gram X Xᵀ on rows), 0: tall
@@ -48,6 +49,7 @@ struct DevProblem {
   // per-phase workgroup prefix (first global workgroup of this problem)
   int32_t wg0[PH_COUNT];
   int32_t ld_x0;               // ld of x0
+  int32_t pad_;                // explicit, so that the struct has no padding bytes (it is hashed)
   // caller buffers (slice stride = rows*cols)
   const void* grad;            // ingest input (grad, or x for ns_batched)
   float* mom;                  // momentum (NULL for ns_batched)
@@ -75,6 +77,7 @@ struct DevProblem {
   float* part_norm;            // [batch][prep_tiles_r*prep_tiles_c]
   float* part_apply;           // [batch][apply_tr*apply_tc]
 };
+static_assert(sizeof(DevProblem) == 112 + 17 * 8, "DevProblem must have no implicit padding");
 
 // Scalars of one launch (passed by value).
 struct LaunchScalars {
@@ -94,6 +97,9 @@ struct LaunchTable {
   float* scal;                 // device, [total_slices][kScalStride]
   int32_t n_probs;
   int32_t total_wg;            // workgroups of this launch
+  uint32_t tag;                // hash of the host-built table: a workgroup whose
+                               // problem entry carries another tag (the workspace
+                               // does not hold this plan's table) exits at once
 };
 
 // ---- the adamw route ----------------------------------------------------
@@ -102,13 +108,14 @@ struct AdamwProblem {
   int32_t grad_bf16;
   int32_t chunks;              // workgroups (kElemChunk elements each)
   int32_t wg0;                 // first workgroup of this tensor
-  int32_t pad;
+  uint32_t tag;                // plan tag (see AdamwTable::tag)
   const void* grad;
   float* param;
   float* m;
   float* v;
   uint16_t* pub;
 };
+static_assert(sizeof(AdamwProblem) == 24 + 5 * 8, "AdamwProblem must have no implicit padding");
 
 struct AdamwScalars {
   float decay;                 // 1 − lr·wd
@@ -124,6 +131,18 @@ struct AdamwTable {
   const int32_t* wg_prefix;    // device, [n_probs + 1]
   int32_t n_probs;
   int32_t total_wg;
+  uint32_t tag;                // as LaunchTable::tag
+};
+
+// One piece of a host-built table, carried to the device in the kernel
+// arguments of a one-workgroup copy kernel: no host buffer has to outlive the
+// call, and a captured graph replays the same bytes.
+constexpr int kChunkWords = 508;        // 2 KiB of kernel arguments per piece
+struct TableChunk {
+  uint32_t* dst;                        // device, 4-byte aligned
+  int32_t n_words;
+  int32_t pad;
+  uint32_t words[kChunkWords];
 };
 
 // Kernel launchers (kernels.hip).  Return 0 or a hipError_t value.
@@ -132,6 +151,9 @@ int launch_phase(int phase, int prec_f32, const LaunchTable& tab, const LaunchSc
 int launch_gemm_nt(const void* A, const void* B, float* C, int64_t M, int64_t N, int64_t K,
                    int64_t lda, int64_t ldb, int64_t ldc, int f32, void* stream);
 int launch_adamw(const AdamwTable& tab, const AdamwScalars& s, void* stream);
+// Copy `bytes` (a multiple of 4) of host data to device memory at `dst`, in
+// kernel arguments of copy kernels enqueued on `stream`.
+int launch_write_table(void* dst, const void* src, size_t bytes, void* stream);
 const char* hip_error_string(int err);
 
 // Phase timing (abi.cpp).

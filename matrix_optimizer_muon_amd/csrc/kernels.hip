@@ -171,6 +171,7 @@ __global__ __launch_bounds__(kThreads) void k_norm(LaunchTable tab, LaunchScalar
   const int bid = blockIdx.x;
   const int p = find_prob(tab.wg_prefix + PH_NORM * (tab.n_probs + 1), tab.n_probs, bid);
   const DevProblem& P = tab.probs[p];
+  if (P.tag != tab.tag) return;
   const int slice = bid - P.wg0[PH_NORM];
   const int cnt = P.prep_tiles_r * P.prep_tiles_c;
   const float total = sum_partials<4>(P.part_norm + (int64_t)slice * cnt, cnt, red);
@@ -201,6 +202,7 @@ __global__ __launch_bounds__(kThreads) void k_ingest(LaunchTable tab, LaunchScal
   const int bid = blockIdx.x;
   const int p = find_prob(tab.wg_prefix + PH_INGEST * (tab.n_probs + 1), tab.n_probs, bid);
   const DevProblem& P = tab.probs[p];
+  if (P.tag != tab.tag) return;
   const int local = bid - P.wg0[PH_INGEST];
   const int per_slice = P.prep_tiles_r * P.prep_tiles_c;
   const int slice = local / per_slice, tt = local % per_slice;
@@ -310,6 +312,7 @@ __global__ __launch_bounds__(kThreads) void k_update(LaunchTable tab, LaunchScal
   const int bid = blockIdx.x;
   const int p = find_prob(tab.wg_prefix + PH_UPDATE * (tab.n_probs + 1), tab.n_probs, bid);
   const DevProblem& P = tab.probs[p];
+  if (P.tag != tab.tag) return;
   const int local = bid - P.wg0[PH_UPDATE];
   const int slice = local / P.chunks, chunk = local % P.chunks;
   const int64_t per = (int64_t)P.rows * P.cols;
@@ -357,6 +360,7 @@ __device__ __forceinline__ void adamw_elem(float& p, float& m, float& v, float g
 __global__ __launch_bounds__(kThreads) void k_adamw(AdamwTable tab, AdamwScalars s) {
   const int bid = blockIdx.x;
   const AdamwProblem& P = tab.probs[find_prob(tab.wg_prefix, tab.n_probs, bid)];
+  if (P.tag != tab.tag) return;
   const int64_t e0 = (int64_t)(bid - P.wg0) * kElemChunk;
   const int64_t e1 = (e0 + kElemChunk < P.numel) ? e0 + kElemChunk : P.numel;
   const gptr<float> pp = glob(P.param);
@@ -1346,6 +1350,7 @@ __global__ __launch_bounds__(kGemmThreads) void k_gemm(LaunchTable tab, LaunchSc
   const int bid = xcd_logical_block<PH == PH_GRAM ? 16 : 32>();
   const int p = find_prob(tab.wg_prefix + PH * (tab.n_probs + 1), tab.n_probs, bid);
   const DevProblem& P = tab.probs[p];
+  if (P.tag != tab.tag) return;      // the workspace holds another plan's table
   const int local = bid - P.wg0[PH];
   const int m = P.m;
 
@@ -1500,6 +1505,14 @@ __global__ __launch_bounds__(kGemmThreads) void k_gemm_plain(GemmArgs g) {
 }
 
 // ---------------------------------------------------------------------------
+// table writer: one workgroup copies one piece of a host-built table from its
+// kernel arguments to device memory
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(kThreads) void k_write_table(TableChunk c) {
+  for (int i = threadIdx.x; i < c.n_words; i += kThreads) glob(c.dst)[i] = c.words[i];
+}
+
+// ---------------------------------------------------------------------------
 // host-side launchers
 // ---------------------------------------------------------------------------
 template <typename K>
@@ -1528,6 +1541,23 @@ static int ensure_lds(int f32) {
   }
   if (e == 0) flag = 1;
   return e;
+}
+
+int launch_write_table(void* dst, const void* src, size_t bytes, void* stream) {
+  TableChunk c;
+  c.pad = 0;
+  const uint32_t* w = (const uint32_t*)src;
+  const size_t words = bytes / 4;
+  for (size_t off = 0; off < words; off += kChunkWords) {
+    const size_t n = words - off < (size_t)kChunkWords ? words - off : (size_t)kChunkWords;
+    c.dst = (uint32_t*)dst + off;
+    c.n_words = (int32_t)n;
+    __builtin_memcpy(c.words, w + off, n * 4);
+    hipLaunchKernelGGL(k_write_table, dim3(1), dim3(kThreads), 0, (hipStream_t)stream, c);
+    const int e = (int)hipGetLastError();
+    if (e) return e;
+  }
+  return 0;
 }
 
 int launch_adamw(const AdamwTable& tab, const AdamwScalars& s, void* stream) {

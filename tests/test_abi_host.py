@@ -32,7 +32,7 @@ def test_library_exports_every_header_function():
     for name in names:
         assert hasattr(L, name), name
     assert sorted(B.EXPORTED) == names
-    assert L.dmuon_abi_version() == 3 == B.ABI_VERSION
+    assert L.dmuon_abi_version() == 4 == B.ABI_VERSION
 
 
 # --------------------------------------------------------------------------
@@ -109,17 +109,30 @@ def desc(ndim=2, shape=(8, 16), dtype=B.F32, base=FAKE, numel_bytes=1 << 20):
 
 def cfg(**kw):
     c = dict(lr=0.02, momentum=0.95, weight_decay=0.01, eps=1e-7, coeffs=(3.4445, -4.775, 2.0315),
-             steps=5, precision="bf16")
+             steps=5, precision="bf16", stream_groups=0)
     c.update(kw)
     return B.make_cfg(c["lr"], c["momentum"], c["weight_decay"], c["eps"], c["coeffs"],
-                      c["steps"], c["precision"])
+                      c["steps"], c["precision"], 1.0, c["stream_groups"])
 
 
-def step(descs, c=None, ws=FAKE + (1 << 40), ws_bytes=1 << 40):
+ENTRY = ("dmuon_muon_step", "dmuon_muon_step_prepare", "dmuon_muon_step_run")
+
+
+def step(descs, c=None, ws=FAKE + (1 << 40), ws_bytes=1 << 40, side=None, n_side=0):
+    """Call all three step entry points with the same arguments; they validate
+    alike, so they must return the same code."""
     arr = (B.Tensor * max(len(descs), 1))(*descs)
     c = c or cfg()
-    return B.lib().dmuon_muon_step(arr, len(descs), ctypes.byref(c), ctypes.c_void_p(ws), ws_bytes,
-                                   None)
+    L = B.lib()
+    rcs = []
+    for name in ENTRY:
+        args = [arr, len(descs), ctypes.byref(c), ctypes.c_void_p(ws), ws_bytes, None]
+        if name != "dmuon_muon_step_prepare":
+            args += [side, n_side]
+        rcs.append(getattr(L, name)(*args))
+    if n_side == 0 and side is None:
+        assert len(set(rcs)) == 1, rcs
+    return rcs[0] if len(set(rcs)) == 1 else rcs
 
 
 def wsize(descs, c=None):
@@ -156,10 +169,51 @@ def test_rejects_bad_arguments():
     c = cfg()
     c.prec = 5
     assert step([desc()], c) == -4
+    assert step([desc()], cfg(stream_groups=5)) == -5
+    assert step([desc()], cfg(stream_groups=-1)) == -5
     arr = (B.Tensor * 1)()
-    assert B.lib().dmuon_muon_step(arr, -1, ctypes.byref(cfg()), None, 0, None) == -3
-    assert B.lib().dmuon_muon_step(None, 1, ctypes.byref(cfg()), None, 0, None) == -1
-    assert B.lib().dmuon_muon_step(arr, 1, None, None, 0, None) == -1
+    assert B.lib().dmuon_muon_step(arr, -1, ctypes.byref(cfg()), None, 0, None, None, 0) == -3
+    assert B.lib().dmuon_muon_step(None, 1, ctypes.byref(cfg()), None, 0, None, None, 0) == -1
+    assert B.lib().dmuon_muon_step(arr, 1, None, None, 0, None, None, 0) == -1
+
+
+def test_rejects_bad_side_streams():
+    two = (ctypes.c_void_p * 2)(0x1000, None)
+    one = (ctypes.c_void_p * 1)(0x1000)
+    L = B.lib()
+    arr = (B.Tensor * 1)(desc())
+    for name in ("dmuon_muon_step", "dmuon_muon_step_run"):
+        fn = getattr(L, name)
+        base = [arr, 1, ctypes.byref(cfg()), ctypes.c_void_p(FAKE + (1 << 40)), 1 << 40, None]
+        assert fn(*base, None, -1) == -5
+        assert fn(*base, None, 1) == -1                 # array missing
+        assert fn(*base, two, 2) == -1                   # NULL entry (the null stream)
+        # a valid stream list passes validation; the call then fails only where it
+        # would touch the GPU, after the forced failure point below
+        os.environ["DMUON_TEST_FAIL_AT"] = "plan"
+        try:
+            assert fn(*base, one, 1) == -8
+        finally:
+            del os.environ["DMUON_TEST_FAIL_AT"]
+
+
+def test_group_count():
+    def groups(descs, c=None):
+        arr = (B.Tensor * max(len(descs), 1))(*descs)
+        out = ctypes.c_int32(-1)
+        rc = B.lib().dmuon_muon_step_groups(arr, len(descs), ctypes.byref(c or cfg()), ctypes.byref(out))
+        return rc, out.value
+    small = [desc(shape=(512, 512), base=FAKE + (i << 24)) for i in range(6)]
+    assert groups(small) == (0, 4)                       # under four rounds of tiles: 4 groups
+    assert groups(small[:2]) == (0, 2)                   # never more than the tensors
+    big = [desc(shape=(8192, 28672), base=FAKE + (i << 34)) for i in range(2)]
+    assert groups(big) == (0, 1)                         # many rounds: one launch sequence
+    assert groups(small, cfg(stream_groups=3)) == (0, 3)
+    assert groups(small, cfg(stream_groups=1)) == (0, 1)
+    assert groups([desc(shape=(0, 4))]) == (0, 0)
+    assert groups(small, cfg(stream_groups=9))[0] == -5
+    # the workspace depends on the group count (per-group tables)
+    assert wsize(small, cfg(stream_groups=1))[1] != wsize(small, cfg(stream_groups=4))[1]
 
 
 def test_rejects_aliasing():
@@ -233,10 +287,24 @@ def test_ns_batched_and_gemm_validation():
     assert L.dmuon_gemm_nt(vp(FAKE), vp(FAKE), vp(FAKE), 4, 4, 10, 64, 64, 4, 2, None) == -4
 
 
-def test_forced_failure_before_enqueue(monkeypatch):
-    monkeypatch.setenv("DMUON_TEST_FAIL_AT", "plan")
-    assert step([desc()]) == -8
-    assert "forced" in B.lib().dmuon_last_error().decode()
+@pytest.mark.parametrize("where", ["plan", "table"])
+def test_forced_failure_before_enqueue(monkeypatch, where):
+    """'plan' fails after validation; 'table' fails the table copy before its
+    first launch: neither makes a HIP call, so both run without a GPU."""
+    monkeypatch.setenv("DMUON_TEST_FAIL_AT", where)
+    L = B.lib()
+    arr = (B.Tensor * 1)(desc())
+    ws = ctypes.c_void_p(FAKE + (1 << 40))
+    assert L.dmuon_muon_step(arr, 1, ctypes.byref(cfg()), ws, 1 << 40, None, None, 0) == -8
+    assert f"DMUON_TEST_FAIL_AT={where}" in L.dmuon_last_error().decode()
+    assert L.dmuon_muon_step_prepare(arr, 1, ctypes.byref(cfg()), ws, 1 << 40, None) == -8
+    vp = ctypes.c_void_p
+    assert L.dmuon_ns_batched(vp(FAKE), 0, vp(FAKE + 4096), 1, 4, 4, 3.4, -4.7, 2.0, 5, 1e-7, 1, 0,
+                              ws, 1 << 40, None) == -8
+    if where == "plan":   # run copies no table: it fails at 'plan' only
+        assert L.dmuon_muon_step_run(arr, 1, ctypes.byref(cfg()), ws, 1 << 40, None, None, 0) == -8
+    # an invalid call still reports its own error first
+    assert L.dmuon_muon_step(arr, 1, ctypes.byref(cfg(steps=99)), ws, 1 << 40, None, None, 0) == -5
     monkeypatch.delenv("DMUON_TEST_FAIL_AT")
 
 
@@ -323,7 +391,8 @@ def test_adamw_aliasing_and_sizes():
     assert rc1 == rc2 == 0 and 0 < s1 < s2
 
 
-def test_adamw_forced_failure(monkeypatch):
-    monkeypatch.setenv("DMUON_TEST_FAIL_AT", "plan")
+@pytest.mark.parametrize("where", ["plan", "table"])
+def test_adamw_forced_failure(monkeypatch, where):
+    monkeypatch.setenv("DMUON_TEST_FAIL_AT", where)
     assert astep([adesc()]) == -8
     monkeypatch.delenv("DMUON_TEST_FAIL_AT")

@@ -43,7 +43,7 @@ def to_dev(td):
             torch.from_numpy(td.master.copy()).to(dev))
 
 
-def gpu_step(tds, precision, steps=5, want_o=True, hp=None):
+def gpu_step(tds, precision, steps=5, want_o=True, hp=None, stream_groups=0):
     hp = dict(HYPER, **(hp or {}))
     devs = [to_dev(td) for td in tds]
     outs = [torch.empty(td.grad.shape, dtype=torch.float32, device="cuda") for td in tds] \
@@ -51,7 +51,7 @@ def gpu_step(tds, precision, steps=5, want_o=True, hp=None):
     mm.muon_step([d[0] for d in devs], [d[1] for d in devs], [d[2] for d in devs],
                  lr=hp["lr"], momentum=hp["mu"], weight_decay=hp["wd"], eps=hp["eps"],
                  coeffs=(hp["a"], hp["b"], hp["c"]), steps=steps, precision=precision,
-                 ns_outs=outs)
+                 ns_outs=outs, stream_groups=stream_groups)
     torch.cuda.synchronize()
     res = []
     for i, d in enumerate(devs):
@@ -226,7 +226,7 @@ def test_step_resume_equals_two_steps():
     assert torch.equal(m, m3) and torch.equal(w, w3)
 
 
-@pytest.mark.parametrize("precision", ["bf16"])
+@pytest.mark.parametrize("precision", ["bf16", "f32"])
 def test_step_layer_d2048_full(precision):
     """The one-layer d = 2048 workload at full size (7 matrices, one grouped launch)."""
     wl = workload("layer_d2048")
@@ -234,24 +234,35 @@ def test_step_layer_d2048_full(precision):
     check_step(tds, precision, label="layer_d2048")
 
 
-def test_step_merged_small_full():
-    """384 small matrices with a decaying spectrum in one grouped call (bf16 path)."""
+@pytest.mark.parametrize("precision", ["bf16", "f32"])
+def test_step_merged_small_full(precision):
+    """384 small matrices with a decaying spectrum in one grouped call."""
     wl = workload("merged_small")
     tds = [make_tensor(wl, t) for t in wl.tensors]
-    check_step(tds, "bf16", label="merged_small")
+    check_step(tds, precision, label="merged_small")
 
 
-def test_stream_groups_do_not_change_results(monkeypatch):
-    """Splitting the tensors over concurrent streams gives the same bits as one sequence."""
+def test_stream_groups_do_not_change_results():
+    """Splitting the tensors over concurrent streams gives the same bits as one
+    sequence, and so do the groups run in order on one stream."""
+    import ctypes
+    from matrix_optimizer_muon_amd import _binding as B
     tds = [make_custom((600, 1000), "bf16", seed=(64, 0), scale=1e-3),
            make_custom((1000, 600), "f32", seed=(64, 1)),
            make_custom((3, 300, 520), "bf16", seed=(64, 2), scale=1e-3),
            make_custom((257, 257), "f32", seed=(64, 3)),
            make_custom((64, 64), "bf16", seed=(64, 4), scale=1e-3)]
-    runs = []
-    for groups in ("1", "3", "4"):
-        monkeypatch.setenv("DMUON_STREAM_GROUPS", groups)
-        runs.append(gpu_step(tds, "bf16"))
+    runs = [gpu_step(tds, "bf16", stream_groups=g) for g in (1, 3, 4)]
+    # four groups, no side streams: the groups run one after another on the stream
+    devs = [to_dev(td) for td in tds]
+    outs = [torch.empty(td.grad.shape, dtype=torch.float32, device="cuda") for td in tds]
+    cfg = B.make_cfg(HYPER["lr"], HYPER["mu"], HYPER["wd"], HYPER["eps"], Q5, 5, "bf16", 1.0, 4)
+    arr, n = B.make_descs([d[0] for d in devs], [d[1] for d in devs], [d[2] for d in devs], outs)
+    ws = B.alloc_workspace(B.muon_step_workspace_size(cfg, (arr, n)), "cuda")
+    B.check(B.lib().dmuon_muon_step(arr, n, ctypes.byref(cfg), ctypes.c_void_p(ws.data_ptr()), ws.numel(),
+                                    B._stream_handle(None), None, 0))
+    torch.cuda.synchronize()
+    runs.append([(d[1].cpu().numpy(), o.cpu().numpy(), d[2].cpu().numpy()) for d, o in zip(devs, outs)])
     for other in runs[1:]:
         for (b0, o0, w0), (b1, o1, w1) in zip(runs[0], other):
             assert np.array_equal(b0, b1) and np.array_equal(o0, o1) and np.array_equal(w0, w1)
@@ -274,16 +285,97 @@ def test_longest_accepted_dims(precision):
     check_step(tds, precision, label="longest dims")
 
 
-def test_graph_capture_is_refused():
-    """A call on a stream that is capturing a graph is rejected before it enqueues
-    anything (its table copy reads a reused host buffer), and the capture and the
-    next plain call are unaffected."""
-    td = make_custom((300, 700), "f32", seed=(68, 0))
-    g_, m_, w_ = to_dev(td)
-    graph = torch.cuda.CUDAGraph()
-    with pytest.raises(RuntimeError, match="capturing a graph"):
-        with torch.cuda.graph(graph):
-            mm.muon_step([g_], [m_], [w_])
+@pytest.mark.parametrize("stream_groups", [1, 3])
+def test_graph_capture_replays_the_step(stream_groups):
+    """A prepared step captured into a graph (with its side streams) and replayed
+    twice gives the same bits as two direct steps; eager work and host
+    synchronisations run between the replays."""
+    tds = [make_custom((600, 1000), "bf16", seed=(68, 0), scale=1e-3),
+           make_custom((1000, 600), "f32", seed=(68, 1)),
+           make_custom((3, 300, 520), "bf16", seed=(68, 2), scale=1e-3)]
+
+    def prepared():
+        devs = [to_dev(td) for td in tds]
+        outs = [torch.zeros(td.grad.shape, dtype=torch.float32, device="cuda") for td in tds]
+        st = mm.MuonStep([d[0] for d in devs], [d[1] for d in devs], [d[2] for d in devs],
+                         ns_outs=outs, stream_groups=stream_groups)
+        return devs, outs, st
+
+    def snap(devs, outs):
+        return [(d[1].cpu().numpy(), o.cpu().numpy(), d[2].cpu().numpy()) for d, o in zip(devs, outs)]
+
+    devs, outs, direct = prepared()
+    assert direct.groups == stream_groups
+    direct()
     torch.cuda.synchronize()
-    assert np.array_equal(m_.cpu().numpy(), td.momentum) and np.array_equal(w_.cpu().numpy(), td.master)
-    check_step([td], "bf16", label="after refused capture")
+    want1 = snap(devs, outs)
+    direct()
+    torch.cuda.synchronize()
+    want2 = snap(devs, outs)
+
+    devs, outs, st = prepared()
+    before = snap(devs, outs)
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        st()
+    torch.cuda.synchronize()
+    for got, exp in zip(snap(devs, outs), before):      # capturing runs nothing
+        assert all(np.array_equal(a, b) for a, b in zip(got, exp))
+    for want in (want1, want2):
+        graph.replay()
+        torch.cuda.synchronize()
+        junk = torch.randn(1 << 20, device="cuda") * 2.0   # eager work between the replays
+        torch.cuda.synchronize()
+        del junk
+        for got, exp in zip(snap(devs, outs), want):
+            assert all(np.array_equal(a, b) for a, b in zip(got, exp))
+
+
+def test_run_needs_its_prepared_tables():
+    """A run on a workspace whose tables belong to other tensors does nothing
+    (every workgroup finds another plan tag and exits)."""
+    import ctypes
+    from matrix_optimizer_muon_amd import _binding as B
+    a = make_custom((300, 500), "f32", seed=(69, 0))
+    b = make_custom((300, 500), "f32", seed=(69, 1))
+    da, db = to_dev(a), to_dev(b)
+    st = mm.MuonStep(list(da[:1]), [da[1]], [da[2]], stream_groups=1)
+    cfg = st.cfg
+    arr, n = B.make_descs([db[0]], [db[1]], [db[2]])
+    ws = st.workspace
+    B.check(B.lib().dmuon_muon_step_run(arr, n, ctypes.byref(cfg), ctypes.c_void_p(ws.data_ptr()),
+                                        ws.numel(), B._stream_handle(None), None, 0))
+    torch.cuda.synchronize()
+    assert np.array_equal(db[1].cpu().numpy(), b.momentum) and np.array_equal(db[2].cpu().numpy(), b.master)
+    st()                         # its own tensors still step
+    torch.cuda.synchronize()
+    assert not np.array_equal(da[2].cpu().numpy(), a.master)
+
+
+@pytest.mark.parametrize("where", ["table", "ingest", "norm", "gram", "square", "apply", "update"])
+def test_failure_between_phases(monkeypatch, where):
+    """DMUON_TEST_FAIL_AT makes the step return DMUON_E_HIP at a phase, with the
+    earlier launches enqueued.  Contract: the gradient is never written; the
+    master, the NS output and the published copy are written only by the last
+    apply (or the update when k = 0), so a failure before it leaves them alone;
+    a later call steps normally."""
+    steps = 0 if where == "update" else 5
+    tds = [make_custom((600, 1000), "bf16", seed=(70, 0), scale=1e-3),
+           make_custom((2, 520, 300), "f32", seed=(70, 1))]
+    devs = [to_dev(td) for td in tds]
+    g0 = [d[0].clone() for d in devs]
+    outs = [torch.full(td.grad.shape, 7.0, device="cuda") for td in tds]
+    pubs = [torch.full(td.grad.shape, 1234, dtype=torch.int16, device="cuda") for td in tds]
+    monkeypatch.setenv("DMUON_TEST_FAIL_AT", where)
+    with pytest.raises(RuntimeError, match=f"DMUON_TEST_FAIL_AT={where}"):
+        mm.muon_step([d[0] for d in devs], [d[1] for d in devs], [d[2] for d in devs], steps=steps,
+                     ns_outs=outs, param_outs=pubs, stream_groups=2)
+    monkeypatch.delenv("DMUON_TEST_FAIL_AT")
+    torch.cuda.synchronize()
+    for td, d, g, o, p in zip(tds, devs, g0, outs, pubs):
+        assert torch.equal(d[0], g)
+        assert np.array_equal(d[2].cpu().numpy(), td.master)
+        assert bool((o == 7.0).all()) and bool((p == 1234).all())
+        if where in ("table", "ingest"):
+            assert np.array_equal(d[1].cpu().numpy(), td.momentum)
+    check_step(tds, "bf16", label=f"after a failure at {where}")
