@@ -12,7 +12,9 @@ import os
 import numpy as np
 
 HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(HERE, "libdmuon_ns.so")
+# DMUON_LIBRARY selects another build of the library (the host-sanitized one of
+# the CPU tests); by default the in-tree build is loaded
+LIB_PATH = os.environ.get("DMUON_LIBRARY") or os.path.join(HERE, "libdmuon_ns.so")
 
 DMUON_OK = 0
 ERRORS = {

@@ -6,7 +6,7 @@
 // communication; the HSDP guide ("what happens underneath", step 3) repeats it.
 // Rank checks follow the MindSpore parameter-grouping page §2.1 / §4.1 (fewer
 // than two dims is an error) and §2.2 / §6 (the matrix is the last two dims).
-#include <hip/hip_runtime.h>
+#include <hip/hip_runtime_api.h>
 
 #include <algorithm>
 #include <cmath>
