@@ -186,6 +186,22 @@ int dmuon_muon_step_run(const dmuon_tensor* tensors, int32_t n_tensors, const dm
                         void* workspace, size_t workspace_bytes, void* stream, void* const* side_streams,
                         int32_t n_side_streams);
 
+/* The same step for callers that cannot allocate device memory (code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc): no
+ * workspace argument, no device allocation and no allocating HIP call.  The
+ * step's scratch (tables, iterate, operand copies, partial sums) lives in a
+ * static device array of the library, 64 MiB per GPU, which each GPU the
+ * library runs on holds until the process ends; a step whose
+ * dmuon_muon_step_workspace_size with stream_groups = 1 exceeds 64 MiB returns
+ * DMUON_E_WORKSPACE before anything is enqueued.  The step runs as one group
+ * on `stream` (cfg->stream_groups must be 0 or 1) and gives the same bits as
+ * dmuon_muon_step.  Every call on a GPU uses that GPU's one array and nothing
+ * in it needs clearing between calls; calls that overlap on one GPU (on
+ * different streams, or from different threads) race on it and must be
+ * ordered by the caller.  Host-side planning uses the C++ heap. */
+int dmuon_muon_step_noalloc(const dmuon_tensor* tensors, int32_t n_tensors, const dmuon_step_cfg* cfg,
+                            void* stream);
+
 /* Bytes of workspace dmuon_ns_batched needs (host only, no HIP call). */
 int dmuon_ns_batched_workspace_size(int64_t batch, int64_t rows, int64_t cols, int32_t prec,
                                     int32_t steps, size_t* bytes);

@@ -31,7 +31,8 @@ F32, BF16 = 0, 1
 PREC = {"bf16": 0, "f32": 1}
 PHASES = ["ingest", "norm", "gram", "square", "apply", "update", "gemm_nt", "adamw"]
 EXPORTED = ["dmuon_muon_step_workspace_size", "dmuon_muon_step_groups", "dmuon_muon_step",
-            "dmuon_muon_step_prepare", "dmuon_muon_step_run", "dmuon_ns_batched_workspace_size",
+            "dmuon_muon_step_prepare", "dmuon_muon_step_run", "dmuon_muon_step_noalloc",
+            "dmuon_ns_batched_workspace_size",
             "dmuon_ns_batched", "dmuon_lpt_assign", "dmuon_adamw_step_workspace_size",
             "dmuon_adamw_step", "dmuon_gemm_nt", "dmuon_phase_timing", "dmuon_phase_timing_read",
             "dmuon_last_error", "dmuon_abi_version"]
@@ -89,6 +90,7 @@ def lib():
     L.dmuon_muon_step.argtypes = [P(Tensor), i32, P(StepCfg), vp, sz, vp, P(vp), i32]
     L.dmuon_muon_step_prepare.argtypes = [P(Tensor), i32, P(StepCfg), vp, sz, vp]
     L.dmuon_muon_step_run.argtypes = [P(Tensor), i32, P(StepCfg), vp, sz, vp, P(vp), i32]
+    L.dmuon_muon_step_noalloc.argtypes = [P(Tensor), i32, P(StepCfg), vp]
     L.dmuon_ns_batched_workspace_size.argtypes = [i64, i64, i64, i32, i32, P(sz)]
     L.dmuon_ns_batched.argtypes = [vp, i32, vp, i64, i64, i64, f32, f32, f32, i32, f32, i32, i32,
                                    vp, sz, vp]
@@ -102,7 +104,7 @@ def lib():
     L.dmuon_last_error.argtypes = []
     L.dmuon_abi_version.restype = i32
     for name in ["dmuon_muon_step_workspace_size", "dmuon_muon_step_groups", "dmuon_muon_step",
-                 "dmuon_muon_step_prepare", "dmuon_muon_step_run",
+                 "dmuon_muon_step_prepare", "dmuon_muon_step_run", "dmuon_muon_step_noalloc",
                  "dmuon_ns_batched_workspace_size", "dmuon_ns_batched", "dmuon_lpt_assign",
                  "dmuon_adamw_step_workspace_size", "dmuon_adamw_step",
                  "dmuon_gemm_nt", "dmuon_phase_timing", "dmuon_phase_timing_read"]:

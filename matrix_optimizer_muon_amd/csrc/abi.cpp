@@ -723,6 +723,34 @@ int dmuon_muon_step(const dmuon_tensor* tensors, int32_t n, const dmuon_step_cfg
                        stream, side_streams, n_side_streams, fa);
 }
 
+int dmuon_muon_step_noalloc(const dmuon_tensor* tensors, int32_t n, const dmuon_step_cfg* cfg, void* stream) {
+  g_err.clear();
+  int e = check_cfg(cfg);
+  if (e) return e;
+  if (cfg->stream_groups > 1) return fail(DMUON_E_CFG, "the allocation-free step runs as one group: stream_groups must be 0 or 1");
+  std::vector<Item> items;
+  std::vector<Range> rs;
+  if ((e = collect_items(tensors, n, items, &rs))) return e;
+  if (items.empty()) return DMUON_OK;
+  if ((e = check_alias(rs))) return e;
+  const int f32 = cfg->prec == DMUON_PREC_F32;
+  GroupPlan sized;
+  if ((e = plan_groups(items, f32, 1, nullptr, sized))) return e;
+  if (sized.bytes > kScratchBytes)
+    return fail(DMUON_E_WORKSPACE, "the allocation-free step needs " + std::to_string(sized.bytes) +
+                                       " bytes of scratch; the library's static scratch holds " +
+                                       std::to_string(kScratchBytes));
+  const FailAt fa = fail_at();
+  if ((e = forced(fa, -2))) return e;
+  void* scr = nullptr;
+  const int r = scratch_region(&scr);
+  if (r) return fail(DMUON_E_HIP, std::string("scratch lookup: ") + hip_error_string(r));
+  GroupPlan gp;
+  if ((e = plan_groups(items, f32, 1, (char*)scr, gp))) return e;
+  if ((e = write_groups(gp, (char*)scr, stream, fa))) return e;
+  return launch_groups(gp, (char*)scr, f32, step_scalars(cfg), cfg->ns_steps, stream, nullptr, 0, fa);
+}
+
 int dmuon_ns_batched_workspace_size(int64_t batch, int64_t rows, int64_t cols, int32_t prec, int32_t steps,
                                     size_t* bytes) {
   g_err.clear();

@@ -16,6 +16,7 @@ constexpr int kPrepTile = 64;          // tile edge of the ingest kernel
 constexpr int kLdAlign = 64;           // operand leading dims are multiples of this
 constexpr int kMaxSteps = 64;          // ns_steps upper bound
 constexpr int kScalStride = 80;        // floats of per-slice scalars (inv, d[0..k])
+constexpr size_t kScratchBytes = (size_t)64 << 20;   // static scratch of the allocation-free step
 
 enum Phase : int {
   PH_INGEST = 0,     // momentum, partial sums of squares, unscaled operand copies
@@ -155,6 +156,9 @@ int launch_adamw(const AdamwTable& tab, const AdamwScalars& s, void* stream);
 // kernel arguments of copy kernels enqueued on `stream`.
 int launch_write_table(void* dst, const void* src, size_t bytes, void* stream);
 const char* hip_error_string(int err);
+// Device address of this GPU's static scratch (kScratchBytes, 256-byte aligned):
+// looked up once per device with hipGetSymbolAddress, then cached.
+int scratch_region(void** ptr);
 
 // Phase timing (abi.cpp).
 void timing_before(int phase, void* stream);

@@ -29,6 +29,8 @@
 #include <hip/hip_runtime.h>
 
 #include <cstdint>
+#include <mutex>
+#include <vector>
 
 #include "internal.hpp"
 
@@ -1623,5 +1625,33 @@ int launch_gemm_nt(const void* A, const void* B, float* C, int64_t M, int64_t N,
 }
 
 const char* hip_error_string(int err) { return hipGetErrorString((hipError_t)err); }
+
+// ---------------------------------------------------------------------------
+// Static scratch of the allocation-free step (dmuon_muon_step_noalloc).  Each
+// GPU the library runs on holds its own copy until the process ends.  In host
+// code `scratch` names a host-side stand-in, not device memory: the device
+// address comes from hipGetSymbolAddress, once per device (with that device
+// current), and only that address is handed to kernels.
+// ---------------------------------------------------------------------------
+static __device__ __align__(256) char scratch[kScratchBytes];
+
+int scratch_region(void** ptr) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return (int)e;
+  static std::mutex mu;
+  static std::vector<void*> by_device;
+  std::lock_guard<std::mutex> lk(mu);
+  if ((int)by_device.size() <= dev) by_device.resize(dev + 1, nullptr);
+  if (!by_device[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return (int)e;
+    if (!p || ((uintptr_t)p & 255)) return (int)hipErrorInvalidSymbol;
+    by_device[dev] = p;
+  }
+  *ptr = by_device[dev];
+  return 0;
+}
 
 }  // namespace dmuon

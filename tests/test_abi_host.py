@@ -308,6 +308,32 @@ def test_forced_failure_before_enqueue(monkeypatch, where):
     monkeypatch.delenv("DMUON_TEST_FAIL_AT")
 
 
+def test_noalloc_validation():
+    """The allocation-free step validates like the others and refuses a step
+    whose scratch would exceed the static 64 MiB before any HIP call."""
+    L = B.lib()
+
+    def noalloc(descs, c=None):
+        arr = (B.Tensor * max(len(descs), 1))(*descs)
+        return L.dmuon_muon_step_noalloc(arr, len(descs), ctypes.byref(c or cfg()), None)
+    assert noalloc([desc(ndim=1, shape=(128,))]) == -2
+    assert noalloc([desc()], cfg(stream_groups=2)) == -5
+    a = desc()
+    a.master = a.momentum
+    assert noalloc([a]) == -7
+    assert noalloc([desc(shape=(0, 7))]) == 0
+    assert noalloc([desc(shape=(8192, 28672), numel_bytes=1 << 30)]) == -6
+    assert "static scratch" in L.dmuon_last_error().decode()
+    rc, need = wsize([desc(shape=(4096, 4096), numel_bytes=1 << 30)], cfg(stream_groups=1))
+    assert rc == 0 and need > 64 << 20
+    assert noalloc([desc(shape=(4096, 4096), numel_bytes=1 << 30)]) == -6
+    os.environ["DMUON_TEST_FAIL_AT"] = "plan"
+    try:
+        assert noalloc([desc(shape=(256, 512))]) == -8      # fits: fails only at the forced point
+    finally:
+        del os.environ["DMUON_TEST_FAIL_AT"]
+
+
 def test_python_wrappers_raise_value_error():
     with pytest.raises(ValueError):
         B.check(-2)
