@@ -83,8 +83,10 @@ typedef enum { DMUON_F32 = 0, DMUON_BF16 = 1 } dmuon_dtype;
 
 /* Arithmetic of the Newton–Schulz contractions.
  * BF16_MFMA: bf16 matrix-core operands, fp32 accumulation; the iterate is
- *            computed in fp32 and stored between iterations rounded (to
- *            nearest even) to its top 24 bits (8 exponent, 15 fraction bits).
+ *            computed in fp32 and kept between iterations as its bf16 operand
+ *            copy plus the remainder quantised to a signed byte, with one
+ *            power-of-two scale per 16 values (about 16 significant bits of
+ *            each group's largest value).
  * F32:       fp32 matrix-core operands and accumulation, fp32 iterate (parity path).
  * Momentum, normalisation, the iterate's axpy and the update are fp32 in both. */
 typedef enum { DMUON_PREC_BF16_MFMA = 0, DMUON_PREC_F32 = 1 } dmuon_prec;

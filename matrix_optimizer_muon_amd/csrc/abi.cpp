@@ -229,8 +229,9 @@ static int build_plan(const std::vector<Item>& items, int prec_f32, Plan& pl, ch
     P.pub = it.pub;
     const int64_t b = it.batch;
     const int64_t prep = (int64_t)P.prep_tiles_r * P.prep_tiles_c;
-    // the iterate: 24-bit values (3 bytes) on the bf16 path, fp32 on the fp32 path
-    P.xf = (float*)carve((size_t)(b * P.apply_tr * P.apply_tc) * kTile * kTile * (prec_f32 ? 4 : 3));
+    // the iterate: fp32 on the fp32 path; on the bf16 path its part below the
+    // bf16 operand copy, one signed byte per value plus one exponent byte per 16
+    P.xf = (float*)carve((size_t)(b * P.apply_tr * P.apply_tc) * kTile * kTile / 16 * (prec_f32 ? 64 : 17));
     if (!it.mom) P.xraw = (float*)carve((size_t)(b * it.rows * P.ld_x) * 4);
     if (prec_f32) {
       P.xg = carve((size_t)(b * P.m * P.ld_n) * esz);

@@ -60,10 +60,12 @@ struct DevProblem {
   const float* x0;             // X₀ before its 1/(‖B‖_F + eps) scale: the momentum
                                // (ld cols), or for ns_batched xraw (ld ld_x)
   // workspace (operand element type = bf16 or fp32 per precision)
-  float* xf;                   // iterate in the apply's register order: per 256×256 tile
-                               // (row-major tile order) kTile² values laid out as
-                               // [wave 8][block 8][16-byte piece][lane 64]; 24-bit values
-                               // (3 pieces per block) on the bf16 path, fp32 (4) on the fp32 one
+  float* xf;                   // iterate in the apply's register order, per 256×256 tile
+                               // (row-major tile order): fp32 path kTile² fp32 values as
+                               // [wave 8][block 8][16-byte piece 4][lane 64]; bf16 path the
+                               // remainder below its bf16 copy, kTile² signed bytes as
+                               // [wave 8][block 8][lane 64][16] then kTile²/16 exponent
+                               // bytes as [wave 8][block 8][lane 64]
   float* xraw;                 // ns_batched only: x in fp32, storage layout rows×ld_x
   void* xs[2];                 // bf16 path: X in storage layout, rows×ld_s with
                                // ld_s = round_up(cols, 64) (ping-pong: the apply reads

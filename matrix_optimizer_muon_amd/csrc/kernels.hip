@@ -30,6 +30,7 @@
 
 #include <cstdint>
 #include <mutex>
+#include <type_traits>
 #include <vector>
 
 #include "internal.hpp"
@@ -559,9 +560,23 @@ __device__ __forceinline__ void mfma_chunk<float>(f32x16_t& acc, const u32x4_t& 
 // s_waitcnt with only lgkmcnt constrained to 0 (vmcnt 63, expcnt 7 = no wait)
 #define DMUON_WAIT_LGKM0() __builtin_amdgcn_s_waitcnt(0xF | (0x3 << 14) | (0x7 << 4))
 
-template <typename T, bool TA = false, bool TB = false>
-__device__ __forceinline__ void gemm_mainloop(const Operands& op, char* smem, f32x16_t (&acc)[4][2]) {
+// The apply's α·X term on the matrix cores (bf16 path).  X enters the apply's
+// contraction as its bf16 operand copy hi; α·hi is α·I times that operand, so
+// in the K stages that cover the tile's own rows (wide: the diagonal block of
+// the B′ operand) or columns (tall: of the B′ operand on the B side) each wave
+// issues extra MFMAs against a diagonal fragment built in registers.  α is split
+// into two bf16 values α1 = bf16(α), α2 = bf16(α − α1), so α1·hi + α2·hi is
+// α·hi to about 2⁻¹⁷ relative; the products are exact and accumulate in fp32.
+struct DiagTerm {
+  int kd0;           // first K stage of the tile's diagonal block
+  uint32_t a1, a2;   // bf16 bit patterns of α1, α2
+};
+
+template <typename T, bool TA = false, bool TB = false, int DIAG = 0>
+__device__ __forceinline__ void gemm_mainloop(const Operands& op, char* smem, f32x16_t (&acc)[4][2],
+                                              const DiagTerm& dg = DiagTerm{0, 0u, 0u}) {
   static_assert(!(TA || TB) || sizeof(T) == 2, "K-major operands are bf16");
+  static_assert(DIAG == 0 || sizeof(T) == 2, "the diagonal term is for bf16 operands");
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);    // wave-uniform
   const int wr = wave >> 2, wc = wave & 3, h = lane >> 5, r32 = lane & 31;
@@ -694,6 +709,20 @@ __device__ __forceinline__ void gemm_mainloop(const Operands& op, char* smem, f3
     // fragment reads complete before the barrier that releases this slot
     DMUON_WAIT_LGKM0();
   };
+  // diagonal fragment of 16-k chunk ss: this lane holds k = 16·ss + 8·h + e (e < 8)
+  // for row (A side) or column (B side) r32; its only nonzero element is k = r32.
+  // e0 passes through an empty asm so that the fragments are built inside the
+  // (rarely taken) diagonal branch instead of being hoisted out of the K loop,
+  // where they would hold registers for the whole contraction.
+  auto diag_frag = [&](int e, uint32_t bits) {
+    const uint32_t v = (e & 1) ? bits << 16 : bits;
+    u32x4_t f;
+    f.x = (unsigned)e < 2u ? v : 0u;
+    f.y = (unsigned)(e - 2) < 2u ? v : 0u;
+    f.z = (unsigned)(e - 4) < 2u ? v : 0u;
+    f.w = (unsigned)(e - 6) < 2u ? v : 0u;
+    return f;
+  };
   auto mfma_phase = [&]() {
     __builtin_amdgcn_s_setprio(1);
 #pragma unroll
@@ -702,6 +731,28 @@ __device__ __forceinline__ void gemm_mainloop(const Operands& op, char* smem, f3
       for (int i = 0; i < 4; ++i)
 #pragma unroll
         for (int j = 0; j < 2; ++j) mfma_chunk<T>(acc[i][j], fa[ss][i], fb[ss][j]);
+    __builtin_amdgcn_s_setprio(0);
+  };
+  // the extra MFMAs of a diagonal stage: block I of the wave's rows (A side) or
+  // columns (B side)
+  auto diag_phase = [&](auto I) {
+    constexpr int b = decltype(I)::value;
+    int e0 = r32 - 8 * h;
+    asm volatile("" : "+v"(e0));
+    __builtin_amdgcn_s_setprio(1);
+#pragma unroll
+    for (int ss = 0; ss < 2; ++ss)
+#pragma unroll
+      for (int p = 0; p < 2; ++p) {
+        const u32x4_t df = diag_frag(e0 - 16 * ss, p ? dg.a2 : dg.a1);
+        if constexpr (DIAG == 1) {
+#pragma unroll
+          for (int j = 0; j < 2; ++j) mfma_chunk<T>(acc[b][j], df, fb[ss][j]);
+        } else {
+#pragma unroll
+          for (int i = 0; i < 4; ++i) mfma_chunk<T>(acc[i][b], fa[ss][i], df);
+        }
+      }
     __builtin_amdgcn_s_setprio(0);
   };
 
@@ -713,8 +764,7 @@ __device__ __forceinline__ void gemm_mainloop(const Operands& op, char* smem, f3
   __builtin_amdgcn_s_barrier();
   if (!lead) __builtin_amdgcn_s_barrier();             // trailing group: one phase late
   __builtin_amdgcn_sched_barrier(0);
-#pragma unroll 1
-  for (int kt = 0; kt < KT; ++kt) {
+  auto step = [&](int kt) {
     mem_phase(kt);
     __builtin_amdgcn_sched_barrier(0);
     __builtin_amdgcn_s_barrier();
@@ -723,6 +773,40 @@ __device__ __forceinline__ void gemm_mainloop(const Operands& op, char* smem, f3
     __builtin_amdgcn_sched_barrier(0);
     __builtin_amdgcn_s_barrier();
     __builtin_amdgcn_sched_barrier(0);
+  };
+  if constexpr (DIAG == 0) {
+#pragma unroll 1
+    for (int kt = 0; kt < KT; ++kt) step(kt);
+  } else {
+    // every wave runs KT steps with the same barriers; its diagonal stages
+    // [kb, kb + nb) (wide: its 4 row blocks, tall: its 2 column blocks) are
+    // unrolled so that each names its accumulator block at compile time
+    constexpr int nb = DIAG == 1 ? 4 : 2;
+    const int kb = dg.kd0 + (DIAG == 1 ? 4 * wr : 2 * wc);
+    const int k1 = kb < KT ? kb : KT;
+#pragma unroll 1
+    for (int kt = 0; kt < k1; ++kt) step(kt);
+    auto dstep = [&](auto I) {
+      const int kt = kb + decltype(I)::value;
+      if (kt >= KT) return;
+      mem_phase(kt);
+      __builtin_amdgcn_sched_barrier(0);
+      __builtin_amdgcn_s_barrier();
+      __builtin_amdgcn_sched_barrier(0);
+      mfma_phase();
+      diag_phase(I);
+      __builtin_amdgcn_sched_barrier(0);
+      __builtin_amdgcn_s_barrier();
+      __builtin_amdgcn_sched_barrier(0);
+    };
+    dstep(std::integral_constant<int, 0>{});
+    dstep(std::integral_constant<int, 1>{});
+    if constexpr (nb == 4) {
+      dstep(std::integral_constant<int, 2>{});
+      dstep(std::integral_constant<int, 3>{});
+    }
+#pragma unroll 1
+    for (int kt = kb + nb < KT ? kb + nb : KT; kt < KT; ++kt) step(kt);
   }
   if (lead) __builtin_amdgcn_s_barrier();              // every wave passes 2·KT + 2 barriers
   // all LDS reads done before the caller reuses LDS
@@ -1021,15 +1105,18 @@ typedef unsigned u32x2_t __attribute__((ext_vector_type(2)));
 // 64·wc + 32·j + r32.  Per block:
 //   X' = xs·(α·X + acc), α = a + b·d + c·d² (xs = 0 for columns past the
 //        matrix, whose accumulators hold finite values read past a row's end).
-//        At t = 0 X is read from the unscaled source x0 (B, storage layout,
-//        4-byte accesses: each wave instruction covers two 128-byte row
-//        segments) and xs = inv; later xs = 1 and X is the stored iterate, kept
-//        in the order of the registers (16-byte pieces per lane, 1 KiB
-//        contiguous per wave instruction): on the bf16 path 24-bit values (the
-//        top 24 bits of the fp32 value, rounded to nearest even), four per three
-//        dwords, so a block moves with 3 loads and 3 stores; on the fp32 path
-//        fp32 values, 4 and 4.  Traffic touched once per phase (the iterate, the
-//        copy, the master weight) uses the nontemporal cache policy.
+//        fp32 path: at t = 0 X is read from the unscaled source x0 (B, storage
+//        layout, 4-byte accesses: each wave instruction covers two 128-byte row
+//        segments) and xs = inv; later xs = 1 and X is the stored fp32 iterate,
+//        kept in the order of the registers (16-byte pieces per lane, 1 KiB
+//        contiguous per wave instruction, 4 loads and 4 stores per block).
+//        bf16 path: X = hi + lo with hi its bf16 operand copy.  The contraction
+//        already added α·hi (diagonal MFMAs, see DiagTerm), so the epilogue adds
+//        α·lo: at t = 0 lo = x0 − bf16(x0) from the fp32 source; later lo is
+//        stored in register order as 16 signed bytes per lane and block (one
+//        16-byte load and store) with a shared exponent byte (enc_lo).
+//        Traffic touched once per phase (the iterate, the copy, the master
+//        weight) uses the nontemporal cache policy.
 //   t < k−1: the storage-layout operand copy (fp32 path: also the transposed
 //        copy); Σ X'² partial
 //   last:  W ← (1 − lr·wd)·W − lr·X', optional copy of X' to the output and
@@ -1041,24 +1128,35 @@ typedef unsigned u32x2_t __attribute__((ext_vector_type(2)));
 // 16-byte pieces of whole rows.  The bf16 path keeps only this storage-layout copy: every
 // bf16 contraction reads it row-major or K-major.  The fp32 path (no K-major
 // reads) stores the row-major and the transposed copy directly.
-template <typename T, bool LAST>
+template <typename T, bool LAST, bool FROM0>
 struct ApplyEpilogue {
-  static constexpr int kAhead = LAST ? 2 : 4;
-  static constexpr int kPre = LAST ? 1 : 3;       // blocks loaded before the contraction
   static constexpr unsigned E = sizeof(T);
-  // dwords per 4 values of the stored iterate: 24-bit values on the bf16 path
-  // (whose operands are bf16 anyway), fp32 on the fp32 path
-  static constexpr int kXWords = E == 2 ? 3 : 4;
+  static constexpr int kAhead = LAST ? 2 : 4;
+  // blocks loaded before the contraction (live across it: two of the fp32 start
+  // blocks on the bf16 path's first iteration, whose contraction also holds the
+  // diagonal term's registers)
+  static constexpr int kPre = LAST ? 1 : (FROM0 && E == 2 ? 2 : 3);
+  // registers per loaded block: 16 fp32 values (the fp32 start X₀ = inv·B at
+  // t = 0, or the fp32 iterate), or q (4 dwords) + exponent on the bf16 path
+  static constexpr int kIn = FROM0 || E != 2 ? 16 : 5;
+  // fp32 path: the iterate in fp32, 4 dwords per 4 values.  bf16 path: the
+  // iterate is its bf16 operand copy hi (storage layout) plus lo = X − hi in
+  // register order, 16 signed bytes per lane and block with one shared
+  // exponent byte: kTile² bytes of q, then kTile²/16 exponent bytes per tile
+  static constexpr int kXWords = 4;
+  static constexpr unsigned kLoBytes = (unsigned)(kTile * kTile);
+  static constexpr int64_t kTileIterBytes = E == 2 ? (int64_t)kTile * kTile * 17 / 16 : (int64_t)kTile * kTile * 4;
 
   __amdgpu_buffer_rsrc_t rx, ri, rw, ro, rd, rt, rp;
   unsigned xi[2], wo[2], dofs[2], tofs[2], po[2];
-  unsigned xb, ldi, ld_s, ld_t, cols;
+  unsigned xb, xe, ldi, ld_s, ld_t, cols;
   unsigned lr0;
   int row0, col0;
-  bool odd, pub_pairs, from0;
+  bool odd, pub_pairs;
+  static constexpr bool from0 = FROM0;
   bool colok[2];                         // the lane's column of block j lies inside the matrix
   bool has_w, has_out, has_pub;          // last apply: which outputs exist (workgroup-uniform)
-  float xin[kAhead][16];
+  float xin[kAhead][kIn];
   float win[LAST ? kAhead : 1][16];
 
   __device__ __forceinline__ ApplyEpilogue(const DevProblem& P, const LaunchScalars& s, int slice, int u,
@@ -1078,12 +1176,13 @@ struct ApplyEpilogue {
 #pragma unroll
     for (int j = 0; j < 2; ++j) colok[j] = lc0 + 32 * j < tcols;
 
-    // the iterate's tile: byte (((wave·8 + blk)·4 + rq)·64 + lane)·16
-    rx = range_rsrc(P.xf + ((int64_t)slice * P.apply_tr * P.apply_tc + u) * (kTile * kTile / 4 * kXWords),
-                    (int64_t)kTile * kTile * kXWords);
-    xb = (unsigned)((wave * 8 * kXWords * 64 + lane) * 16);
+    // the iterate's tile: fp32 byte (((wave·8 + blk)·4 + rq)·64 + lane)·16; bf16
+    // path q at ((wave·8 + blk)·64 + lane)·16, exponent at kLoBytes + (wave·8 + blk)·64 + lane
+    rx = range_rsrc((const char*)P.xf + ((int64_t)slice * P.apply_tr * P.apply_tc + u) * kTileIterBytes,
+                    kTileIterBytes);
+    xb = (unsigned)((wave * 8 * (E == 2 ? 1 : kXWords) * 64 + lane) * 16);
+    xe = kLoBytes + (unsigned)(wave * 8 * 64 + lane);
     // the X₀ read at t = 0: the unscaled source in storage layout
-    from0 = s.t == 0;
     ldi = (unsigned)P.ld_x0;
     ri = range_rsrc(from0 ? P.x0 + ((int64_t)slice * rows + row0) * ldi : nullptr, (int64_t)trows * ldi * 4);
 #pragma unroll
@@ -1139,45 +1238,58 @@ struct ApplyEpilogue {
 
   // byte offset of 16-byte piece q of block blk in the iterate's tile
   __device__ __forceinline__ unsigned xq(int blk, int q) const {
-    return xb + (unsigned)((blk * kXWords + q) * 64 * 16);
+    return xb + (unsigned)((blk * (E == 2 ? 1 : kXWords) + q) * 64 * 16);
   }
 
-  // 24-bit iterate (bf16 path): the top 24 bits of the fp32 value, rounded to
-  // nearest even; four values go into three dwords
-  static __device__ __forceinline__ uint32_t enc24(float f) {
-    const uint32_t u = __float_as_uint(f);
-    return (u + 0x7Fu + ((u >> 8) & 1u)) >> 8;
-  }
-  static __device__ __forceinline__ void pack24(const float (&v)[16], uint32_t (&w)[12]) {
+  // bf16 path: lo = X − hi of the lane's 16 values in a block, as signed bytes
+  // q with one shared exponent byte eb (0: all zero).  With mx = max |lo| and
+  // eb its biased fp32 exponent, q = rint(lo · 2^(133 − eb)) has |q| ≤ 127 and
+  // lo = q · 2^(eb − 133) to within 2^(eb − 134) ≤ mx · 2⁻⁸; since |lo| is at most
+  // half a bf16 ulp of X, the stored X keeps about 16 significant bits of the
+  // block's largest value.
+  static __device__ __forceinline__ void enc_lo(const float (&lo)[16], u32x4_t& q, uint32_t& eb) {
+    float mx = 0.f;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) mx = fmaxf(mx, fabsf(lo[r]));
+    const uint32_t e = (__float_as_uint(mx) >> 23) & 0xFFu;
+    eb = e < 8u ? 0u : e;
+    const float sc = eb ? __uint_as_float((260u - eb) << 23) : 0.f;
+    uint32_t w[4];
 #pragma unroll
     for (int g = 0; g < 4; ++g) {
-      const uint32_t c0 = enc24(v[4 * g]), c1 = enc24(v[4 * g + 1]), c2 = enc24(v[4 * g + 2]),
-                     c3 = enc24(v[4 * g + 3]);
-      w[3 * g] = c0 | (c1 << 24);
-      w[3 * g + 1] = (c1 >> 8) | (c2 << 16);
-      w[3 * g + 2] = (c2 >> 16) | (c3 << 8);
+      uint32_t acc = 0u;
+#pragma unroll
+      for (int b = 0; b < 4; ++b) {
+        const int qi = (int)__builtin_rintf(fminf(fmaxf(lo[4 * g + b] * sc, -127.f), 127.f));
+        acc |= ((uint32_t)qi & 0xFFu) << (8 * b);
+      }
+      w[g] = acc;
     }
+    q = u32x4_t{w[0], w[1], w[2], w[3]};
   }
-  static __device__ __forceinline__ void unpack24(const float (&in)[16], float (&x)[16]) {
+  static __device__ __forceinline__ void dec_lo(const float (&in)[kIn], float (&lo)[16]) {
+    const uint32_t eb = __float_as_uint(in[4]);
+    const float sc = eb ? __uint_as_float((eb - 6u) << 23) : 0.f;
 #pragma unroll
-    for (int g = 0; g < 4; ++g) {
-      const uint32_t d0 = __float_as_uint(in[3 * g]), d1 = __float_as_uint(in[3 * g + 1]),
-                     d2 = __float_as_uint(in[3 * g + 2]);
-      x[4 * g] = __uint_as_float((d0 & 0xFFFFFFu) << 8);
-      x[4 * g + 1] = __uint_as_float(((d0 >> 24) | ((d1 & 0xFFFFu) << 8)) << 8);
-      x[4 * g + 2] = __uint_as_float(((d1 >> 16) | ((d2 & 0xFFu) << 16)) << 8);
-      x[4 * g + 3] = __uint_as_float(d2 & 0xFFFFFF00u);
+    for (int r = 0; r < 16; ++r) {
+      const int qi = __builtin_amdgcn_sbfe((int)__float_as_uint(in[r >> 2]), 8 * (r & 3), 8);
+      lo[r] = (float)qi * sc;
     }
   }
 
   __device__ __forceinline__ void load_blk(int blk, int slot) {
     const int i = blk >> 1, j = blk & 1;
-    if (from0) {
+    if constexpr (FROM0) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const unsigned rr = (unsigned)(32 * i + 8 * (r >> 2) + (r & 3));
         xin[slot][r] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(ri, (int)(xi[j] + rr * ldi * 4u), 0, 2));  // nt
       }
+    } else if constexpr (E == 2) {
+      const f32x4_t w = __builtin_amdgcn_raw_buffer_load_b128(rx, (int)xq(blk, 0), 0, 2);     // nontemporal
+      xin[slot][0] = w.x; xin[slot][1] = w.y; xin[slot][2] = w.z; xin[slot][3] = w.w;
+      xin[slot][4] = __uint_as_float((uint32_t)__builtin_amdgcn_raw_buffer_load_b8(
+          rx, (int)(xe + (unsigned)(blk * 64)), 0, 2));
     } else {
 #pragma unroll
       for (int q = 0; q < kXWords; ++q) {
@@ -1228,11 +1340,18 @@ struct ApplyEpilogue {
       const int slot = blk % kAhead;
       const int i = blk >> 1, j = blk & 1;
       float v[16];
-      if (kXWords == 3 && !from0) {
-        unpack24(xin[slot], v);
+      if constexpr (E == 2) {
+        // the accumulator already holds α·hi (diagonal MFMAs); add α·lo, with
+        // lo = X₀ − bf16(X₀) at t = 0 (the operand was bf16 of the fp32 start)
+        if constexpr (FROM0) {
+#pragma unroll
+          for (int r = 0; r < 16; ++r) v[r] = xin[slot][r] - bf16_to_f32(f32_to_bf16(xin[slot][r]));
+        } else {
+          dec_lo(xin[slot], v);
+        }
       } else {
 #pragma unroll
-        for (int r = 0; r < 16; ++r) v[r] = xin[slot][r];
+        for (int r = 0; r < 16; ++r) v[r] = xin[slot][r % kIn];
       }
       // columns past the matrix are zero: a K-major operand can feed them values
       // read past a row's end, which must not reach Σ X'² or any store
@@ -1276,14 +1395,24 @@ struct ApplyEpilogue {
       } else {
 #pragma unroll
         for (int r = 0; r < 16; ++r) sq = fmaf(v[r], v[r], sq);
-        if constexpr (kXWords == 3) {
-          uint32_t w[12];
-          pack24(v, w);
+        if constexpr (E == 2) {
+          // hi = bf16(X') goes into the LDS-staged copy; v keeps lo = X' − hi
 #pragma unroll
-          for (int q = 0; q < 3; ++q)
-            // nontemporal (cache policy 2): read again only by the next apply
-            __builtin_amdgcn_raw_buffer_store_b128(u32x4_t{w[4 * q], w[4 * q + 1], w[4 * q + 2], w[4 * q + 3]}, rx,
-                                                   (int)xq(blk, q), 0, 2);
+          for (int rq = 0; rq < 4; ++rq)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {           // one 16-bit value per row
+              const unsigned cb = (lc0 + 32u * (unsigned)j) * 2u;            // byte of the column in its row
+              const unsigned r = lr0 + 32u * (unsigned)i + 8u * (unsigned)rq + (unsigned)e;
+              const uint16_t hb = f32_to_bf16(v[4 * rq + e]);
+              *(__attribute__((address_space(3))) uint16_t*)(smem + r * 512u + ((((cb >> 4) ^ row_swz(r)) << 4) | (cb & 15u))) = hb;
+              v[4 * rq + e] -= bf16_to_f32(hb);
+            }
+          u32x4_t q;
+          uint32_t eb;
+          enc_lo(v, q, eb);
+          // nontemporal (cache policy 2): read again only by the next apply
+          __builtin_amdgcn_raw_buffer_store_b128(q, rx, (int)xq(blk, 0), 0, 2);
+          __builtin_amdgcn_raw_buffer_store_b8((uint8_t)eb, rx, (int)(xe + (unsigned)(blk * 64)), 0, 2);
         } else {
 #pragma unroll
           for (int rq = 0; rq < 4; ++rq)
@@ -1301,24 +1430,15 @@ struct ApplyEpilogue {
             __builtin_amdgcn_raw_buffer_store_b128(w4, rt, (int)o, 0, 0);
           }
         }
-        // row-major copy
+        // fp32 path: the row-major copy (the bf16 copy went into LDS above)
+        if constexpr (E != 2) {
 #pragma unroll
-        for (int rq = 0; rq < 4; ++rq) {
-          if constexpr (E == 2) {
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {           // one 16-bit value per row
-              const unsigned cb = (lc0 + 32u * (unsigned)j) * 2u;            // byte of the column in its row
-              const unsigned r = lr0 + 32u * (unsigned)i + 8u * (unsigned)rq + (unsigned)e;
-              *(__attribute__((address_space(3))) uint16_t*)(smem + r * 512u + ((((cb >> 4) ^ row_swz(r)) << 4) | (cb & 15u))) =
-                  f32_to_bf16(v[4 * rq + e]);
-            }
-          } else {
+          for (int rq = 0; rq < 4; ++rq)
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
               const unsigned rr = (unsigned)(32 * i + 8 * rq + e);
               buf_st(rd, dofs[j] + rr * ld_s * E, v[4 * rq + e]);
             }
-          }
         }
       }
       if (blk + kAhead < 8) load_blk(blk + kAhead, slot);
@@ -1343,7 +1463,7 @@ struct ApplyEpilogue {
   }
 };
 
-template <typename T, int PH, bool LAST>
+template <typename T, int PH, bool LAST, bool FROM0 = false>
 __global__ __launch_bounds__(kGemmThreads) void k_gemm(LaunchTable tab, LaunchScalars s) {
   extern __shared__ __align__(16) char smem[];
   __shared__ float red[kGemmWaves];
@@ -1450,10 +1570,22 @@ __global__ __launch_bounds__(kGemmThreads) void k_gemm(LaunchTable tab, LaunchSc
 
   f32x16_t acc[4][2];
   if constexpr (PH == PH_APPLY) {
-    ApplyEpilogue<T, LAST> epi(P, s, slice, u, row0, col0);
+    ApplyEpilogue<T, LAST, FROM0> epi(P, s, slice, u, row0, col0);
     epi.prefetch();
-    if constexpr (kKmaj) gemm_mainloop<T, false, true>(op, smem, acc);
-    else gemm_mainloop<T>(op, smem, acc);
+    if constexpr (kKmaj) {
+      // α·hi on the matrix cores: the diagonal block of the B′ side, A for a
+      // wide slice (rows of the tile), B for a tall one (its columns)
+      const float alpha = s.a + s.b * d + s.c * d * d;
+      DiagTerm dg;
+      const uint16_t a1 = f32_to_bf16(alpha);
+      dg.a1 = a1;
+      dg.a2 = f32_to_bf16(alpha - bf16_to_f32(a1));
+      dg.kd0 = (P.wide ? row0 : col0) / 32;
+      if (P.wide) gemm_mainloop<T, false, true, 1>(op, smem, acc, dg);
+      else gemm_mainloop<T, false, true, 2>(op, smem, acc, dg);
+    } else {
+      gemm_mainloop<T>(op, smem, acc);
+    }
     epi.finish(P, s, acc, slice, u, d, xs, smem, red);
   } else {
     if constexpr (!kKmaj || PH == PH_SQUARE) {
@@ -1531,14 +1663,18 @@ static int ensure_lds(int f32) {
   if (f32) {
     e |= set_lds(k_gemm<float, PH_GRAM, false>);
     e |= set_lds(k_gemm<float, PH_SQUARE, false>);
-    e |= set_lds(k_gemm<float, PH_APPLY, false>);
-    e |= set_lds(k_gemm<float, PH_APPLY, true>);
+    e |= set_lds(k_gemm<float, PH_APPLY, false, false>);
+    e |= set_lds(k_gemm<float, PH_APPLY, true, false>);
+    e |= set_lds(k_gemm<float, PH_APPLY, false, true>);
+    e |= set_lds(k_gemm<float, PH_APPLY, true, true>);
     e |= set_lds(k_gemm_plain<float>);
   } else {
     e |= set_lds(k_gemm<uint16_t, PH_GRAM, false>);
     e |= set_lds(k_gemm<uint16_t, PH_SQUARE, false>);
-    e |= set_lds(k_gemm<uint16_t, PH_APPLY, false>);
-    e |= set_lds(k_gemm<uint16_t, PH_APPLY, true>);
+    e |= set_lds(k_gemm<uint16_t, PH_APPLY, false, false>);
+    e |= set_lds(k_gemm<uint16_t, PH_APPLY, true, false>);
+    e |= set_lds(k_gemm<uint16_t, PH_APPLY, false, true>);
+    e |= set_lds(k_gemm<uint16_t, PH_APPLY, true, true>);
     e |= set_lds(k_gemm_plain<uint16_t>);
   }
   if (e == 0) flag = 1;
@@ -1591,10 +1727,22 @@ int launch_phase(int phase, int prec_f32, const LaunchTable& tab, const LaunchSc
       if (prec_f32) hipLaunchKernelGGL((k_gemm<float, PH_SQUARE, false>), grid, gblock, kGemmLds, st, tab, s);
       else hipLaunchKernelGGL((k_gemm<uint16_t, PH_SQUARE, false>), grid, gblock, kGemmLds, st, tab, s);
       break;
-    case PH_APPLY:
-      if (prec_f32) { if (s.last) hipLaunchKernelGGL((k_gemm<float, PH_APPLY, true>), grid, gblock, kGemmLds, st, tab, s); else hipLaunchKernelGGL((k_gemm<float, PH_APPLY, false>), grid, gblock, kGemmLds, st, tab, s); }
-      else { if (s.last) hipLaunchKernelGGL((k_gemm<uint16_t, PH_APPLY, true>), grid, gblock, kGemmLds, st, tab, s); else hipLaunchKernelGGL((k_gemm<uint16_t, PH_APPLY, false>), grid, gblock, kGemmLds, st, tab, s); }
+    case PH_APPLY: {
+      // instantiations by (last apply, first iteration: X₀ read from its fp32 source)
+      const int v = (s.last ? 1 : 0) | (s.t == 0 ? 2 : 0);
+      if (prec_f32) {
+        if (v == 0) hipLaunchKernelGGL((k_gemm<float, PH_APPLY, false, false>), grid, gblock, kGemmLds, st, tab, s);
+        else if (v == 1) hipLaunchKernelGGL((k_gemm<float, PH_APPLY, true, false>), grid, gblock, kGemmLds, st, tab, s);
+        else if (v == 2) hipLaunchKernelGGL((k_gemm<float, PH_APPLY, false, true>), grid, gblock, kGemmLds, st, tab, s);
+        else hipLaunchKernelGGL((k_gemm<float, PH_APPLY, true, true>), grid, gblock, kGemmLds, st, tab, s);
+      } else {
+        if (v == 0) hipLaunchKernelGGL((k_gemm<uint16_t, PH_APPLY, false, false>), grid, gblock, kGemmLds, st, tab, s);
+        else if (v == 1) hipLaunchKernelGGL((k_gemm<uint16_t, PH_APPLY, true, false>), grid, gblock, kGemmLds, st, tab, s);
+        else if (v == 2) hipLaunchKernelGGL((k_gemm<uint16_t, PH_APPLY, false, true>), grid, gblock, kGemmLds, st, tab, s);
+        else hipLaunchKernelGGL((k_gemm<uint16_t, PH_APPLY, true, true>), grid, gblock, kGemmLds, st, tab, s);
+      }
       break;
+    }
     case PH_UPDATE: hipLaunchKernelGGL(k_update, grid, block, 0, st, tab, s); break;
     case PH_NORM: hipLaunchKernelGGL(k_norm, grid, block, 0, st, tab, s); break;
     default: return (int)hipErrorInvalidValue;
