@@ -146,10 +146,11 @@ int dmuon_muon_step_workspace_size(const dmuon_tensor* tensors, int32_t n_tensor
                                    const dmuon_step_cfg* cfg, size_t* bytes);
 
 /* Number of work groups the step splits these tensors into (host only, no HIP
- * call): cfg->stream_groups if set, else 4 when the workload is under four
- * rounds of 256×256 output tiles on the 256 compute units (the groups' tail
- * rounds then overlap each other's contractions), else 1; never more than the
- * number of non-empty tensors. */
+ * call): cfg->stream_groups if set, else 4 when the apply phase is short (under
+ * 1024 rounds of 32-wide K stages of 256×256 output tiles on the 256 compute
+ * units: the groups' tail rounds, epilogues and launch gaps then overlap each
+ * other's contractions), else 1; never more than the number of non-empty
+ * tensors. */
 int dmuon_muon_step_groups(const dmuon_tensor* tensors, int32_t n_tensors, const dmuon_step_cfg* cfg,
                            int32_t* groups);
 

@@ -313,22 +313,26 @@ static int launch_plan(const Plan& pl, char* ws, int prec_f32, const LaunchScala
 // ---------------------------------------------------------------------------
 constexpr int kMaxGroups = 4;
 
-// Group count from the rounds of apply tiles on the 256 CUs of an MI355X (a
-// fixed count keeps the workspace size a host-only computation).  Measured, ms
-// per step with 1 / 2 / 3 / 4 groups:
-// * below 4 rounds: four groups, whose tail rounds and epilogues overlap each
-//   other's contractions (one d=2048 layer: 2.61 / 2.46 / 2.47 / 2.42);
+// Group count from the length of the apply phase on the 256 CUs of an MI355X,
+// in rounds of 32-wide K stages (Σ tiles · stages / 256; a fixed count keeps the
+// workspace size a host-only computation).  Measured, ms per step with
+// 1 / 2 / 3 / 4 groups on caller-owned side streams:
+// * short phases (under 1024 stage-rounds): four groups, whose tail rounds,
+//   epilogues and launch gaps overlap each other's contractions (one d = 2048
+//   layer, 196 stage-rounds: 2.51 / 2.34 / 2.36 / 2.31; 384 matrices of 512² and
+//   256×1024, 80 stage-rounds: 2.50 / 2.27 / 2.26 / 2.26);
 // * otherwise one: the tails are a small share, and one launch sequence keeps
 //   the operand panels of neighbouring tiles together in each XCD's L2 (Llama
-//   d=4096 share: 58.2 / 60.2; MLP/MoE mix of 8192-wide matrices and 1408-wide
-//   experts: 116.1 / 122.0; 384 small matrices: 2.74 / 2.76).
+//   d = 4096 share, 6304 stage-rounds: 58.2 / 60.2; MLP/MoE mix, 14864:
+//   116.1 / 122.0).
 constexpr int kCusAssumed = 256;
 
 // requested: the cfg's stream_groups (0: the rule above).
 static int group_count(const std::vector<Item>& items, int requested) {
-  double tiles = 0;
-  for (const Item& it : items) tiles += (double)it.batch * cdiv(it.rows, kTile) * cdiv(it.cols, kTile);
-  const int g = requested >= 1 ? requested : (tiles < 4.0 * kCusAssumed ? 4 : 1);
+  double stages = 0;
+  for (const Item& it : items)
+    stages += (double)it.batch * cdiv(it.rows, kTile) * cdiv(it.cols, kTile) * cdiv(std::min(it.rows, it.cols), 32);
+  const int g = requested >= 1 ? requested : (stages < 1024.0 * kCusAssumed ? 4 : 1);
   return std::min<int>(g, (int)items.size());
 }
 
