@@ -49,6 +49,11 @@
  *   "plan" (before anything is enqueued), "table" (the table copy) or a phase
  *   name ("ingest", "norm", "gram", "square", "apply", "update", "adamw": that
  *   phase's first launch, the earlier launches being enqueued).
+ * - DMUON_DEBUG_SYNC (environment, for debugging; set and not "0") waits for
+ *   each launch to finish before the next is enqueued, so a call returns only
+ *   when its work is done, and returns DMUON_E_HIP naming the launch ("table"
+ *   or a phase name) whose wait reported an error.  The wait is skipped on a
+ *   stream under graph capture.  Results are unchanged.
  * - Return value: DMUON_OK or a negative DMUON_E_* code; dmuon_last_error()
  *   then gives a message (thread-local, valid until the next call on the thread).
  * - After DMUON_E_HIP (a HIP launch/copy failed after validation) the contents

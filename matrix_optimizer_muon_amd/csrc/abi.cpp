@@ -96,36 +96,55 @@ static uint32_t fnv1a(const char* p, size_t n) {
   return h;
 }
 
-// Forced failures for the failure-handling tests: DMUON_TEST_FAIL_AT names the
-// point at which a valid call returns DMUON_E_HIP as a failed HIP call would:
-// "plan" (after validation, before anything is enqueued), "table" (the table
-// copy), or a phase name (that phase's first launch; earlier launches are
-// enqueued).
-struct FailAt {
-  int where = -3;   // -3 none, -2 plan, -1 table, else a phase id
+// Per-call debugging switches, read from the environment once per call.
+//
+// DMUON_TEST_FAIL_AT (failure-handling tests) names the point at which a valid
+// call returns DMUON_E_HIP as a failed HIP call would: "plan" (after
+// validation, before anything is enqueued), "table" (the table copy), or a
+// phase name (that phase's first launch; earlier launches are enqueued).
+//
+// DMUON_DEBUG_SYNC (set and not "0") waits for every launch to finish before
+// the next is enqueued and returns DMUON_E_HIP naming the launch whose wait
+// reported an error, so an asynchronous fault is tied to its phase.  The wait
+// is skipped on a stream under graph capture, where it is not allowed.
+static const char* const kPhaseNames[PH_COUNT] = {"ingest", "norm",   "gram",    "square",
+                                                  "apply",  "update", "gemm_nt", "adamw"};
+struct CallEnv {
+  int where = -3;     // -3 none, -2 plan, -1 table, else a phase id
+  bool sync = false;  // DMUON_DEBUG_SYNC
 };
-static FailAt fail_at() {
-  FailAt f;
+static CallEnv call_env() {
+  CallEnv f;
+  const char* d = std::getenv("DMUON_DEBUG_SYNC");
+  f.sync = d && *d && std::strcmp(d, "0") != 0;
   const char* v = std::getenv("DMUON_TEST_FAIL_AT");
   if (!v) return f;
-  static const char* names[PH_COUNT] = {"ingest", "norm", "gram", "square", "apply", "update", "gemm_nt", "adamw"};
   if (std::strcmp(v, "plan") == 0) f.where = -2;
   else if (std::strcmp(v, "table") == 0) f.where = -1;
   for (int i = 0; i < PH_COUNT; ++i)
-    if (std::strcmp(v, names[i]) == 0) f.where = i;
+    if (std::strcmp(v, kPhaseNames[i]) == 0) f.where = i;
   return f;
 }
-static int forced(const FailAt& f, int where) {
+static int forced(const CallEnv& f, int where) {
   if (f.where != where) return DMUON_OK;
   return fail(DMUON_E_HIP, std::string("forced failure (DMUON_TEST_FAIL_AT=") + std::getenv("DMUON_TEST_FAIL_AT") + ")");
 }
+static int settle(const CallEnv& f, void* stream, const char* what) {
+  if (!f.sync) return DMUON_OK;
+  hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+  int r = (int)hipStreamIsCapturing((hipStream_t)stream, &cs);
+  if (r == 0 && cs != hipStreamCaptureStatusNone) return DMUON_OK;
+  if (r == 0) r = (int)hipStreamSynchronize((hipStream_t)stream);
+  if (r) return fail(DMUON_E_HIP, std::string(what) + " (DMUON_DEBUG_SYNC): " + hip_error_string(r));
+  return DMUON_OK;
+}
 
-static int write_table(void* dst, const std::vector<char>& host, void* stream, const FailAt& fa) {
+static int write_table(void* dst, const std::vector<char>& host, void* stream, const CallEnv& fa) {
   int e = forced(fa, -1);
   if (e) return e;
   e = launch_write_table(dst, host.data(), host.size(), stream);
   if (e) return fail(DMUON_E_HIP, std::string("table copy: ") + hip_error_string(e));
-  return DMUON_OK;
+  return settle(fa, stream, "table");
 }
 
 // ---------------------------------------------------------------------------
@@ -267,7 +286,7 @@ static int build_plan(const std::vector<Item>& items, int prec_f32, Plan& pl, ch
 
 // Enqueue the phases of one plan whose tables are in the workspace at ws.
 static int launch_plan(const Plan& pl, char* ws, int prec_f32, const LaunchScalars& base_s, int steps,
-                       void* stream, const FailAt& fa) {
+                       void* stream, const CallEnv& fa) {
   LaunchTable tab;
   tab.probs = (const DevProblem*)ws;
   tab.wg_prefix = (const int32_t*)(ws + pl.off_prefix);
@@ -280,7 +299,7 @@ static int launch_plan(const Plan& pl, char* ws, int prec_f32, const LaunchScala
     tab.total_wg = (int32_t)pl.total_wg[ph];
     const int r = launch_phase(ph, prec_f32, tab, s, stream);
     if (r) return fail(DMUON_E_HIP, std::string("launch failed: ") + hip_error_string(r));
-    return DMUON_OK;
+    return settle(fa, stream, kPhaseNames[ph]);
   };
   int e;
   LaunchScalars s = base_s;
@@ -381,7 +400,7 @@ static int plan_groups(const std::vector<Item>& items, int prec_f32, int request
 }
 
 // Copy every group's tables into the workspace, on the caller's stream.
-static int write_groups(GroupPlan& gp, char* ws, void* stream, const FailAt& fa) {
+static int write_groups(GroupPlan& gp, char* ws, void* stream, const CallEnv& fa) {
   for (size_t g = 0; g < gp.plans.size(); ++g) {
     const std::vector<char> host = seal(gp.plans[g]);
     const int e = write_table(ws + gp.offs[g], host, stream, fa);
@@ -395,7 +414,7 @@ static int write_groups(GroupPlan& gp, char* ws, void* stream, const FailAt& fa)
 // fork from `stream` and join back to it through events made for this call and
 // released before it returns (HIP keeps a recorded event's pending work alive).
 static int launch_groups(GroupPlan& gp, char* ws, int prec_f32, const LaunchScalars& s, int steps, void* stream,
-                         void* const* side, int n_side, const FailAt& fa) {
+                         void* const* side, int n_side, const CallEnv& fa) {
   const int G = (int)gp.plans.size();
   for (Plan& pl : gp.plans) (void)seal(pl);       // the tags the kernels expect
   const int used = n_side > 0 ? std::min(G - 1, n_side) : 0;
@@ -694,7 +713,7 @@ int dmuon_muon_step_prepare(const dmuon_tensor* tensors, int32_t n, const dmuon_
   GroupPlan gp;
   int e = prepare_step(tensors, n, cfg, workspace, workspace_bytes, items, gp);
   if (e || items.empty()) return e;
-  const FailAt fa = fail_at();
+  const CallEnv fa = call_env();
   if ((e = forced(fa, -2))) return e;
   return write_groups(gp, (char*)workspace, stream, fa);
 }
@@ -707,7 +726,7 @@ int dmuon_muon_step_run(const dmuon_tensor* tensors, int32_t n, const dmuon_step
   std::vector<Item> items;
   GroupPlan gp;
   if ((e = prepare_step(tensors, n, cfg, workspace, workspace_bytes, items, gp)) || items.empty()) return e;
-  const FailAt fa = fail_at();
+  const CallEnv fa = call_env();
   if ((e = forced(fa, -2))) return e;
   return launch_groups(gp, (char*)workspace, cfg->prec == DMUON_PREC_F32, step_scalars(cfg), cfg->ns_steps,
                        stream, side_streams, n_side_streams, fa);
@@ -721,7 +740,7 @@ int dmuon_muon_step(const dmuon_tensor* tensors, int32_t n, const dmuon_step_cfg
   std::vector<Item> items;
   GroupPlan gp;
   if ((e = prepare_step(tensors, n, cfg, workspace, workspace_bytes, items, gp)) || items.empty()) return e;
-  const FailAt fa = fail_at();
+  const CallEnv fa = call_env();
   if ((e = forced(fa, -2))) return e;
   if ((e = write_groups(gp, (char*)workspace, stream, fa))) return e;
   return launch_groups(gp, (char*)workspace, cfg->prec == DMUON_PREC_F32, step_scalars(cfg), cfg->ns_steps,
@@ -745,7 +764,7 @@ int dmuon_muon_step_noalloc(const dmuon_tensor* tensors, int32_t n, const dmuon_
     return fail(DMUON_E_WORKSPACE, "the allocation-free step needs " + std::to_string(sized.bytes) +
                                        " bytes of scratch; the library's static scratch holds " +
                                        std::to_string(kScratchBytes));
-  const FailAt fa = fail_at();
+  const CallEnv fa = call_env();
   if ((e = forced(fa, -2))) return e;
   void* scr = nullptr;
   const int r = scratch_region(&scr);
@@ -804,7 +823,7 @@ int dmuon_ns_batched(const void* x, int32_t x_dtype, float* out, int64_t batch, 
   const uintptr_t wlo = (uintptr_t)workspace, whi = wlo + pl.bytes;
   for (const Range& r : rs)
     if (r.lo < whi && wlo < r.hi) return fail(DMUON_E_ALIAS, "workspace overlaps x or out");
-  const FailAt fa = fail_at();
+  const CallEnv fa = call_env();
   if ((e = forced(fa, -2))) return e;
   Plan real;
   if ((e = build_plan(items, f32, real, (char*)workspace))) return e;
@@ -849,7 +868,7 @@ int dmuon_adamw_step(const dmuon_adamw_tensor* tensors, int32_t n, const dmuon_a
   const uintptr_t wlo = (uintptr_t)workspace, whi = wlo + pl.bytes;
   for (const Range& r : rs)
     if (r.lo < whi && wlo < r.hi) return fail(DMUON_E_ALIAS, "workspace overlaps a tensor buffer");
-  const FailAt fa = fail_at();
+  const CallEnv fa = call_env();
   if ((e = forced(fa, -2))) return e;
   char* ws = (char*)workspace;
   if ((e = write_table(ws, seal(pl), stream, fa))) return e;
@@ -876,7 +895,7 @@ int dmuon_adamw_step(const dmuon_adamw_tensor* tensors, int32_t n, const dmuon_a
   if ((e = forced(fa, PH_ADAMW))) return e;
   const int r = launch_adamw(tab, s, stream);
   if (r) return fail(DMUON_E_HIP, std::string("launch failed: ") + hip_error_string(r));
-  return DMUON_OK;
+  return settle(fa, stream, "adamw");
 }
 
 int dmuon_gemm_nt(const void* A, const void* B, float* C, int64_t M, int64_t N, int64_t K, int64_t lda, int64_t ldb,
@@ -896,7 +915,7 @@ int dmuon_gemm_nt(const void* A, const void* B, float* C, int64_t M, int64_t N, 
   }
   const int r = launch_gemm_nt(A, B, C, M, N, K == 0 ? 1 : K, lda, ldb, ldc, dtype == DMUON_F32, stream);
   if (r) return fail(DMUON_E_HIP, std::string("launch failed: ") + hip_error_string(r));
-  return DMUON_OK;
+  return settle(call_env(), stream, "gemm_nt");
 }
 
 int dmuon_phase_timing(int32_t enable) {

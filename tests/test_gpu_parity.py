@@ -379,3 +379,44 @@ def test_failure_between_phases(monkeypatch, where):
         if where in ("table", "ingest"):
             assert np.array_equal(d[1].cpu().numpy(), td.momentum)
     check_step(tds, "bf16", label=f"after a failure at {where}")
+
+
+def test_debug_sync_changes_nothing(monkeypatch):
+    """DMUON_DEBUG_SYNC waits after every launch: the step, the batched NS and
+    the AdamW route give the same bits as without it, and a step captured into
+    a graph with it set (the waits are skipped there) replays to the same bits."""
+    tds = [make_custom((600, 1000), "bf16", seed=(71, 0), scale=1e-3),
+           make_custom((3, 300, 520), "f32", seed=(71, 1))]
+    x = torch.from_numpy(make_custom((2, 300, 700), "f32", seed=(71, 2)).grad.copy()).cuda()
+
+    def adamw_run():
+        g = torch.randn(5000, generator=torch.Generator().manual_seed(71)).cuda()
+        p, m, v = torch.ones(5000, device="cuda"), torch.zeros(5000, device="cuda"), torch.zeros(5000, device="cuda")
+        mm.adamw_step([p], [g], [m], [v], lr=1e-3, step=1)
+        torch.cuda.synchronize()
+        return p.cpu().numpy(), m.cpu().numpy(), v.cpu().numpy()
+
+    want_step = gpu_step(tds, "bf16", stream_groups=2)
+    want_ns = mm.ns_batched(x, coeffs=Q5, steps=5, eps=HYPER["eps"]).cpu().numpy()
+    want_adamw = adamw_run()
+    monkeypatch.setenv("DMUON_DEBUG_SYNC", "1")
+    got_step = gpu_step(tds, "bf16", stream_groups=2)
+    got_ns = mm.ns_batched(x, coeffs=Q5, steps=5, eps=HYPER["eps"]).cpu().numpy()
+    got_adamw = adamw_run()
+    for w, g in zip(want_step, got_step):
+        assert all(np.array_equal(a, b) for a, b in zip(w, g))
+    assert np.array_equal(want_ns, got_ns)
+    assert all(np.array_equal(a, b) for a, b in zip(want_adamw, got_adamw))
+
+    devs = [to_dev(td) for td in tds]
+    outs = [torch.zeros(td.grad.shape, dtype=torch.float32, device="cuda") for td in tds]
+    st = mm.MuonStep([d[0] for d in devs], [d[1] for d in devs], [d[2] for d in devs], ns_outs=outs,
+                     stream_groups=2)
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        st()
+    graph.replay()
+    torch.cuda.synchronize()
+    for w, d, o in zip(want_step, devs, outs):
+        assert np.array_equal(w[0], d[1].cpu().numpy()) and np.array_equal(w[1], o.cpu().numpy())
+        assert np.array_equal(w[2], d[2].cpu().numpy())
