@@ -25,6 +25,10 @@ pass (``--stream-groups 1`` makes both passes alike, which is the configuration
 the committed rocprofv3 kernel summaries are taken on).  ``--publish`` also writes the
 bf16 published copy of every updated master inside the step.
 
+``--graph`` captures the prepared step of the first pass into a HIP graph and
+times its replays instead (one graph launch per step), which shows what the
+launches themselves cost on small workloads.
+
 ``--route adamw`` measures the ``adamw`` route instead: one ``dmuon_adamw_step``
 over the workload's 1-D parameters per step; ``value`` is elements per second
 and the roofline is HBM bandwidth against algorithmic bytes (gradient read,
@@ -368,6 +372,8 @@ def main():
                     help="also write the bf16 published copy of the updated parameters")
     ap.add_argument("--stream-groups", type=int, default=0,
                     help="concurrent stream groups of the value pass (0: the library's choice)")
+    ap.add_argument("--graph", action="store_true",
+                    help="value pass: capture one prepared step into a HIP graph and time its replays")
     ap.add_argument("--copy-probe", type=int, default=0,
                     help="only run a plain device copy of this many bytes (counter calibration)")
     args = ap.parse_args()
@@ -428,10 +434,19 @@ def main():
         mm.phase_timing(False)
         return ev0.elapsed_time(ev1) / args.steps, wall, mm.phase_timing_read()
 
+    def graphed(prepared):
+        # the step's launches (side streams included) recorded once, replayed
+        # as one graph launch per step on the stream
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            prepared()
+        torch.cuda.synchronize()
+        return lambda st: graph.replay()
+
     # pass 1: throughput in the library's launch configuration
     first = prepare(args.stream_groups)
     groups_used = first.groups
-    ms_step, wall, _ = timed(first, False)
+    ms_step, wall, _ = timed(graphed(first) if args.graph else first, False)
     del first
     slices = n_slices(ts)
     flops = ns_flops(ts, HYPER["steps"])
@@ -492,7 +507,7 @@ def main():
         "tflops_effective": round(tflops, 2),
         "pct_bf16_peak": round(100 * tflops / PEAK_BF16_TFLOPS, 2),
         "config": {"workload": args.workload, "matrices": slices, "shapes": shapes,
-                   "stream_groups": groups_used,
+                   "stream_groups": groups_used, "graph": bool(args.graph),
                    "ns_steps": HYPER["steps"], "grad_dtype": ts[0].grad_dtype,
                    "effective_gflop_per_step": round(flops / 1e9, 1), "publish": bool(args.publish)},
         "roofline": roof,
