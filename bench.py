@@ -89,6 +89,21 @@ def measured_traffic(kernel, workload_name):
         return None
 
 
+def peak_clock_mhz(device_index):
+    """The device's peak shader clock (hipDeviceGetAttribute with
+    hipDeviceAttributeClockRate, value 5 in ROCm 7's hip_runtime_api.h, in kHz),
+    read through the HIP runtime torch has already loaded (same soname)."""
+    import ctypes
+    try:
+        hip = ctypes.CDLL("libamdhip64.so.7")
+    except OSError:
+        return None
+    v = ctypes.c_int(0)
+    if hip.hipDeviceGetAttribute(ctypes.byref(v), ctypes.c_int(5), ctypes.c_int(device_index)) != 0:
+        return None
+    return round(v.value / 1000.0, 1)
+
+
 def copy_probe(nbytes):
     """A plain device-to-device copy of known size (counter calibration)."""
     import torch
@@ -521,7 +536,8 @@ def main():
                                              if p in phases) / args.steps, 4) if phases else None,
         "ms_per_step_one_stream": None if ms_alone is None else round(ms_alone, 4),
         "wall_s_timed": round(wall, 3),
-        "device": {"name": props.name, "cus": props.multi_processor_count},
+        "device": {"name": props.name, "cus": props.multi_processor_count,
+                   "peak_clock_mhz": peak_clock_mhz(dev.index)},
     }
     print(json.dumps(line), flush=True)
 

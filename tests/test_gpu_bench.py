@@ -35,4 +35,5 @@ def test_bench_line(graph):
     roof = line["roofline"]
     assert roof["bound"] == "mfma" and roof["unit"] == "TFLOP/s" and 0 < roof["frac"] < 1
     assert abs(roof["frac"] - roof["achieved"] / roof["peak"]) < 1e-3
-    print(f"graph={graph}: {line['ms_per_step']} ms per step", flush=True)
+    assert line["device"]["cus"] > 0 and line["device"]["peak_clock_mhz"] > 0
+    print(f"graph={graph}: {line['ms_per_step']} ms per step on {line['device']}", flush=True)
