@@ -420,3 +420,50 @@ def test_debug_sync_changes_nothing(monkeypatch):
     for w, d, o in zip(want_step, devs, outs):
         assert np.array_equal(w[0], d[1].cpu().numpy()) and np.array_equal(w[1], o.cpu().numpy())
         assert np.array_equal(w[2], d[2].cpu().numpy())
+
+
+def test_calls_on_a_side_stream():
+    """The step, the batched NS and the AdamW route enqueued on a side stream
+    give the same bits as on the current stream.  Right after each call, the
+    current stream allocates and fills memory of the workspace's size, which the
+    caching allocator would hand out from the call's workspace if that were not
+    tied to the side stream."""
+    tds = [make_custom((600, 1000), "bf16", seed=(72, 0), scale=1e-3),
+           make_custom((3, 300, 520), "f32", seed=(72, 1))]
+    x_np = make_custom((2, 300, 700), "f32", seed=(72, 2)).grad
+    want_step = gpu_step(tds, "bf16", stream_groups=2)
+    x = torch.from_numpy(x_np.copy()).cuda()
+    want_ns = mm.ns_batched(x, coeffs=Q5, steps=5, eps=HYPER["eps"]).cpu().numpy()
+
+    def adamw_args():
+        g = torch.randn(70000, generator=torch.Generator().manual_seed(72)).cuda()
+        return [torch.ones(70000, device="cuda")], [g], [torch.zeros(70000, device="cuda")], \
+            [torch.zeros(70000, device="cuda")]
+    a = adamw_args()
+    mm.adamw_step(*a, lr=1e-3, step=1)
+    torch.cuda.synchronize()
+    want_adamw = [t[0].cpu().numpy() for t in (a[0], a[2], a[3])]
+
+    side = torch.cuda.Stream()
+    devs = [to_dev(td) for td in tds]
+    outs = [torch.empty(td.grad.shape, dtype=torch.float32, device="cuda") for td in tds]
+    x = torch.from_numpy(x_np.copy()).cuda()
+    a = adamw_args()
+    side.wait_stream(torch.cuda.current_stream())
+    nbytes = mm.muon_step_workspace_size([d[0] for d in devs], [d[1] for d in devs], [d[2] for d in devs],
+                                         ns_outs=outs, stream_groups=2)
+    mm.muon_step([d[0] for d in devs], [d[1] for d in devs], [d[2] for d in devs], ns_outs=outs,
+                 stream_groups=2, stream=side)
+    bait = [torch.full((nbytes // 4 + 1,), 3.0, device="cuda") for _ in range(2)]
+    out_ns = mm.ns_batched(x, coeffs=Q5, steps=5, eps=HYPER["eps"], stream=side)
+    bait += [torch.full((1 << 22,), 5.0, device="cuda") for _ in range(2)]
+    mm.adamw_step(*a, lr=1e-3, step=1, stream=side)
+    bait += [torch.full((1 << 20,), 7.0, device="cuda") for _ in range(2)]
+    torch.cuda.synchronize()
+    del bait
+    for w, d, o in zip(want_step, devs, outs):
+        assert np.array_equal(w[0], d[1].cpu().numpy()) and np.array_equal(w[1], o.cpu().numpy())
+        assert np.array_equal(w[2], d[2].cpu().numpy())
+    assert np.array_equal(want_ns, out_ns.cpu().numpy())
+    for w, t in zip(want_adamw, (a[0], a[2], a[3])):
+        assert np.array_equal(w, t[0].cpu().numpy())
