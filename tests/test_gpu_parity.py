@@ -192,6 +192,27 @@ def test_step_other_k(steps):
     check_step(tds, "bf16", steps=steps, label=f"k={steps}")
 
 
+@pytest.mark.parametrize("precision", ["bf16", "f32"])
+def test_step_other_hyperparameters(precision):
+    """Other lr, momentum, weight decay, eps and polynomial (the shift form and
+    the fused update take them as plain scalars), and μ = 0 (B = G)."""
+    tds = [make_custom((300, 700), "f32", seed=(73, 0)),
+           make_custom((2, 520, 300), "bf16", seed=(73, 1), scale=1e-3)]
+    check_step(tds, precision, hp=dict(lr=0.1, mu=0.9, wd=0.1, eps=1e-5, a=2.0, b=-1.5, c=0.5),
+               label="other hyper-parameters")
+    check_step(tds, precision, hp=dict(mu=0.0), label="mu = 0")
+
+
+@pytest.mark.parametrize("precision", ["bf16", "f32"])
+def test_step_more_iterations(precision):
+    """k = 8 with the quintic, whose bf16 error grows with k (about 1e-2 at
+    k = 8 in the numpy emulation), and k = 12 with a milder polynomial."""
+    tds = [make_custom((300, 700), "f32", seed=(74, 0)),
+           make_custom((700, 300), "bf16", seed=(74, 1), scale=1e-3)]
+    check_step(tds, precision, steps=8, label="k = 8")
+    check_step(tds, precision, steps=12, hp=dict(a=2.0, b=-1.5, c=0.5), label="k = 12, (2, -1.5, 0.5)")
+
+
 def test_step_zero_gradient():
     td = make_custom((300, 500), "f32", seed=(63, 0), nonzero_momentum=False)
     td.grad[:] = 0

@@ -107,3 +107,20 @@ def test_shift_matters_on_gaussian():
     shift = rel(ns_bf16_path(G, *Q, K, EPS, iterate="bits", iterate_bits=32, shift=True), want)
     print(f"no shift {no_shift:.2e}, shift {shift:.2e}")
     assert no_shift > 2 * shift
+
+
+def test_error_growth_with_the_iteration_count():
+    """The quintic does not converge (its fixed band is about 0.7–1.1), so each
+    iteration adds its bf16 rounding and the error grows with k: within the
+    2e-2 bound at k = 8 with margin (about 1e-2), and still under it at k = 16
+    on the reduced single-matrix case; a polynomial with a stable fixed point
+    at 1, (2, −1.5, 0.5), keeps it near 1e-3 at k = 16."""
+    G = case_input(0, (256, 512), "f32", "gauss", 1.0)
+    errs = {}
+    for k in (5, 8, 16):
+        errs[k] = rel(ns_bf16_path(G, *Q, k, EPS), oracle.newton_schulz(G, *Q, k, EPS))
+    mild = rel(ns_bf16_path(G, 2.0, -1.5, 0.5, 16, EPS), oracle.newton_schulz(G, 2.0, -1.5, 0.5, 16, EPS))
+    print(f"quintic k=5 {errs[5]:.2e}, k=8 {errs[8]:.2e}, k=16 {errs[16]:.2e}; (2, -1.5, 0.5) k=16 {mild:.2e}")
+    assert errs[5] < errs[8] < errs[16] < 2e-2
+    assert errs[8] < 1.5e-2
+    assert mild < 3e-3
