@@ -213,6 +213,77 @@ def test_step_more_iterations(precision):
     check_step(tds, precision, steps=12, hp=dict(a=2.0, b=-1.5, c=0.5), label="k = 12, (2, -1.5, 0.5)")
 
 
+def fp32_plain_ns(G, steps=5):
+    """The pages' map X ← aX + b(XXᵀ)X + c(XXᵀ)²X evaluated in plain numpy
+    float32 (no shift, no tiling): the yardstick for what fp32 arithmetic itself
+    reaches on inputs whose rounding noise the map amplifies."""
+    f = np.float32
+    X = np.asarray(G, dtype=f)
+    if X.shape[0] > X.shape[1]:
+        return fp32_plain_ns(X.T, steps).T
+    X = X / (f(np.sqrt(np.sum(X.astype(np.float64) ** 2))) + f(HYPER["eps"]))
+    for _ in range(steps):
+        A = X @ X.T
+        X = f(Q5[0]) * X + (f(Q5[1]) * A + f(Q5[2]) * (A @ A)) @ X
+    return X
+
+
+@pytest.mark.parametrize("precision", ["bf16", "f32"])
+def test_step_degenerate_spectra(precision):
+    """Gradients whose singular values are mostly zero (rank 1, rank 2 with
+    distinct values) or all equal (orthonormal rows), wide and tall.  On a
+    rank-deficient input the map multiplies rounding noise in the null space by
+    p'(0) = a per iteration (a⁵ ≈ 490), so fp32 arithmetic itself misses 1e-4
+    there: the fp32 path is held to twice the error of a plain float32
+    evaluation of the same map (and never looser than needed: ≥ 1e-4 only when
+    that evaluation is); the bf16 path to the usual 2e-2."""
+    rng = np.random.default_rng([75, 0])
+    tds = []
+    for k, shape in enumerate([(300, 700), (700, 300), (256, 512)]):
+        td = make_custom(shape, "f32", seed=(75, k), nonzero_momentum=False)
+        m, n = shape
+        if k == 0:
+            G = np.outer(rng.standard_normal(m), rng.standard_normal(n))
+        elif k == 1:
+            U, _ = np.linalg.qr(rng.standard_normal((m, 2)))
+            V, _ = np.linalg.qr(rng.standard_normal((n, 2)))
+            G = (U * np.array([3.0, 1.0])) @ V.T
+        else:
+            Q, _ = np.linalg.qr(rng.standard_normal((n, m)))
+            G = Q.T
+        td.grad[...] = G.astype(np.float32)
+        tds.append(td)
+    got = gpu_step(tds, precision)
+    for td, (B1, O, W1) in zip(tds, got):
+        Bref, Oref, _ = oracle.muon_step(td.grad, td.momentum, td.master, lr=HYPER["lr"], mu=HYPER["mu"],
+                                         wd=HYPER["wd"], eps=HYPER["eps"], a=Q5[0], b=Q5[1], c=Q5[2], steps=5)
+        e_o = rel(O, Oref)
+        tol = TOL_NS["bf16"] if precision == "bf16" else max(TOL_NS["f32"], 2 * rel(fp32_plain_ns(td.grad), Oref))
+        print(f"degenerate {td.spec.shape} {precision}: O {e_o:.2e} (bound {tol:.2e})", flush=True)
+        assert rel(B1, Bref) <= 1e-6
+        assert e_o <= tol, (td.spec.shape, e_o, tol)
+        assert rel(W1, oracle.decay_update(td.master, O, HYPER["lr"], HYPER["wd"])) <= 1e-6
+
+
+@pytest.mark.parametrize("precision", ["bf16", "f32"])
+@pytest.mark.parametrize("stream_groups", [1, 2])
+def test_nan_stays_in_its_slice(precision, stream_groups):
+    """Slices are independent: a NaN in one slice of a batched gradient turns
+    that slice's NS output and master into NaN and leaves every other slice and
+    tensor bit-identical to the run without it."""
+    tds = [make_custom((3, 300, 520), "f32", seed=(76, 0)),
+           make_custom((600, 1000), "bf16", seed=(76, 1), scale=1e-3)]
+    clean = gpu_step(tds, precision, stream_groups=stream_groups)
+    tds[0].grad[1, 17, 33] = np.nan
+    dirty = gpu_step(tds, precision, stream_groups=stream_groups)
+    for part in range(3):                      # momentum, NS output, master
+        assert np.array_equal(clean[0][part][[0, 2]], dirty[0][part][[0, 2]])
+        assert np.array_equal(clean[1][part], dirty[1][part])
+    assert np.isnan(dirty[0][1][1]).all() and np.isnan(dirty[0][2][1]).all()
+    b = dirty[0][0][1]
+    assert np.isnan(b[17, 33]) and np.isnan(b).sum() == 1     # the momentum update is element-wise
+
+
 def test_step_zero_gradient():
     td = make_custom((300, 500), "f32", seed=(63, 0), nonzero_momentum=False)
     td.grad[:] = 0
