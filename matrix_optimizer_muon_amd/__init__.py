@@ -2,7 +2,8 @@
 
 Python face of libdmuon_ns (C ABI in ``include/dmuon_ns.h``).  The functions
 below only marshal arguments: momentum, normalisation, Newton–Schulz and the
-update all run in the library's HIP kernels on the caller's current stream.
+update all run in the library's HIP kernels, on the caller's current stream
+unless a ``stream`` is given.
 
     muon_step(grads, momenta, masters, lr=0.02, momentum=0.95, ...)
     adamw_step(params, grads, exp_avgs, exp_avg_sqs, step=1, ...)  # the "adamw" route
@@ -30,10 +31,6 @@ def load_library():
 
 def abi_version() -> int:
     return int(_b.lib().dmuon_abi_version())
-
-
-def _cfg(lr, momentum, weight_decay, eps, coeffs, steps, precision):
-    return _b.make_cfg(lr, momentum, weight_decay, eps, coeffs, steps, precision)
 
 
 def muon_step_workspace_size(grads, momenta, masters, *, steps=5, precision="bf16",
@@ -262,10 +259,12 @@ def gemm_nt(A, B, K=None, stream=None):
     M, lda = A.shape
     N, ldb = B.shape
     K = lda if K is None else K
-    C = torch.empty((M, N), dtype=torch.float32, device=A.device)
+    st = _b.resolve_stream(stream)
+    with torch.cuda.stream(st):
+        C = torch.empty((M, N), dtype=torch.float32, device=A.device)
     _b.check(_b.lib().dmuon_gemm_nt(ctypes.c_void_p(A.data_ptr()), ctypes.c_void_p(B.data_ptr()),
                                     ctypes.c_void_p(C.data_ptr()), M, N, K, lda, ldb, N,
-                                    _b._dtype_code(A), _b._stream_handle(stream)))
+                                    _b._dtype_code(A), ctypes.c_void_p(st.cuda_stream)))
     return C
 
 
