@@ -284,6 +284,54 @@ def test_nan_stays_in_its_slice(precision, stream_groups):
     assert np.isnan(b[17, 33]) and np.isnan(b).sum() == 1     # the momentum update is element-wise
 
 
+def _emulated_ns_error(td):
+    """Relative error of the bf16 path's designed rounding (numpy emulation,
+    tests/bf16_emulation.py) on this tensor's momentum buffer, per slice."""
+    from bf16_emulation import ns_bf16_path
+    Bf = (np.float32(HYPER["mu"]) * td.momentum + td.grad).astype(np.float32)
+    want = oracle.newton_schulz_batched(Bf, *Q5, 5, HYPER["eps"]) if Bf.ndim == 3 else \
+        oracle.newton_schulz(Bf, *Q5, 5, HYPER["eps"])
+    got = np.stack([ns_bf16_path(x, *Q5, 5, HYPER["eps"]) for x in Bf]) if Bf.ndim == 3 else \
+        ns_bf16_path(Bf, *Q5, 5, HYPER["eps"])
+    return rel(got, want)
+
+
+def _check_many(tds, precision, label):
+    """Every tensor against the oracle.  On the bf16 path a tensor with only a
+    handful of singular values can exceed the workloads' 2e-2 through the
+    designed rounding alone (the emulation reproduces the error), so one that
+    does is held to 1.5 times the emulated error of the same input."""
+    got = gpu_step(tds, precision)
+    worst = [0.0, 0.0, 0.0]
+    over = 0
+    for td, (B1, O, W1) in zip(tds, got):
+        Bref, Oref, _ = oracle.muon_step(td.grad, td.momentum, td.master, lr=HYPER["lr"], mu=HYPER["mu"],
+                                         wd=HYPER["wd"], eps=HYPER["eps"], a=Q5[0], b=Q5[1], c=Q5[2], steps=5)
+        e_b, e_o = rel(B1, Bref), rel(O, Oref)
+        e_w = rel(W1, oracle.decay_update(td.master, O, HYPER["lr"], HYPER["wd"]))
+        assert e_b <= 1e-6 and e_w <= 1e-6, (label, td.spec.shape, e_b, e_w)
+        if e_o > TOL_NS[precision]:
+            assert precision == "bf16", (label, td.spec.shape, e_o)
+            bound = 1.5 * _emulated_ns_error(td)
+            assert e_o <= bound, (label, td.spec.shape, e_o, bound)
+            over += 1
+        worst = [max(worst[0], e_b), max(worst[1], e_o), max(worst[2], e_w)]
+    print(f"{label} {precision}: worst B {worst[0]:.2e} O {worst[1]:.2e} W {worst[2]:.2e}; "
+          f"{over} tensors above {TOL_NS[precision]:.0e}, each within 1.5x its emulated error", flush=True)
+
+
+@pytest.mark.parametrize("precision", ["bf16", "f32"])
+def test_many_slices_and_many_tensors(precision):
+    """Counts far beyond the workloads': 20000 wide 3×5 slices and 5000 tall
+    7×2 slices in two batched tensors (one tile per slice, tens of thousands
+    of workgroups per phase), then 1200 separate tiny tensors in one call
+    (a table of several hundred KiB, written in a few hundred chunks)."""
+    _check_many([make_custom((20000, 3, 5), "f32", seed=(77, 0)),
+                 make_custom((5000, 7, 2), "bf16", seed=(77, 1), scale=1e-3)], precision, "20000 + 5000 slices")
+    _check_many([make_custom((5 + i % 7, 9 + i % 5), "f32", seed=(78, i)) for i in range(1200)], precision,
+                "1200 tensors")
+
+
 def test_step_zero_gradient():
     td = make_custom((300, 500), "f32", seed=(63, 0), nonzero_momentum=False)
     td.grad[:] = 0
