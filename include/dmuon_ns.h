@@ -308,6 +308,43 @@ int dmuon_adamw_step(const dmuon_adamw_tensor* tensors, int32_t n_tensors, const
 int dmuon_gemm_nt(const void* A, const void* B, float* C, int64_t M, int64_t N, int64_t K,
                   int64_t lda, int64_t ldb, int64_t ldc, int32_t dtype, void* stream);
 
+/* Where one slice's intermediates sit in a step workspace (a test hook for the
+ * per-phase checks of the contraction kernels).  Host only, no HIP call: the
+ * call validates the arguments as dmuon_muon_step does, lays the plan out on
+ * `workspace` (the layout dmuon_muon_step_prepare and dmuon_muon_step use for
+ * the same tensors and cfg) and reports device addresses inside it, which it
+ * never dereferences.  `tensor` indexes `tensors`, `slice` its leading dim
+ * (0 for a 2-D tensor).  After a step with cfg.ns_steps = k ≥ 1 the buffers
+ * hold:
+ *   x_copy   the operand copy the first Gram read: bf16 path, bf16(B) of the
+ *            new momentum in the tensor's own layout (x_rows = rows, x_ld ≥
+ *            cols, x_oriented = 0); fp32 path, the oriented X₀ before its scale,
+ *            m × n (x_rows = m, x_ld ≥ n, x_oriented = 1);
+ *   a_prime  A′ = s²·X Xᵀ − d·I of the last Gram, m × m, row stride ld_m (both
+ *            triangles), element type of the path (elem_bytes 2: bf16, 4: fp32),
+ *            with s = inv at t = 0 and 1 later;
+ *   b_prime  B′ = (b + 2cd)·A′ + c·A′² of the last square, same layout;
+ *   scalars  fp32 [inv, d_0, d_1, …, d_{k−1}] with inv = 1/(‖B‖_F + eps) and
+ *            d_t the shift of iteration t.
+ * m = min(rows, cols), n = max; wide = 1 when rows ≤ cols.  DMUON_E_SHAPE if
+ * tensor or slice is out of range. */
+typedef struct {
+  const void* x_copy;
+  int64_t x_rows, x_ld;
+  int32_t x_oriented;
+  int32_t elem_bytes;
+  const void* a_prime;
+  const void* b_prime;
+  int64_t ld_m;
+  const float* scalars;
+  int32_t m, n, wide;
+  int32_t reserved;
+} dmuon_debug_slice;
+
+int dmuon_debug_slice_buffers(const dmuon_tensor* tensors, int32_t n_tensors, const dmuon_step_cfg* cfg,
+                              void* workspace, size_t workspace_bytes, int32_t tensor, int64_t slice,
+                              dmuon_debug_slice* out);
+
 /* Phase timing for profiling (off by default).  enable = 1: every later kernel
  * launch of the library is bracketed by two hipEvents on its stream; enable = 0
  * stops it.  dmuon_phase_timing_read waits for the recorded events, writes for
@@ -322,7 +359,7 @@ int dmuon_phase_timing_read(double* ms, int64_t* count, int32_t n);
 const char* dmuon_last_error(void);
 
 /* ABI version (bumped on any change of a signature, a struct or a documented
- * numbering such as the phases above): 4. */
+ * numbering such as the phases above): 5. */
 int32_t dmuon_abi_version(void);
 
 #ifdef __cplusplus

@@ -35,8 +35,8 @@ EXPORTED = ["dmuon_muon_step_workspace_size", "dmuon_muon_step_groups", "dmuon_m
             "dmuon_ns_batched_workspace_size",
             "dmuon_ns_batched", "dmuon_lpt_assign", "dmuon_adamw_step_workspace_size",
             "dmuon_adamw_step", "dmuon_gemm_nt", "dmuon_phase_timing", "dmuon_phase_timing_read",
-            "dmuon_last_error", "dmuon_abi_version"]
-ABI_VERSION = 4
+            "dmuon_debug_slice_buffers", "dmuon_last_error", "dmuon_abi_version"]
+ABI_VERSION = 5
 
 
 class DmuonError(Exception):
@@ -56,6 +56,14 @@ class StepCfg(ctypes.Structure):
                 ("a", ctypes.c_float), ("b", ctypes.c_float), ("c", ctypes.c_float),
                 ("ns_steps", ctypes.c_int32), ("prec", ctypes.c_int32),
                 ("grad_scale", ctypes.c_float), ("stream_groups", ctypes.c_int32)]
+
+
+class DebugSlice(ctypes.Structure):
+    _fields_ = [("x_copy", ctypes.c_void_p), ("x_rows", ctypes.c_int64), ("x_ld", ctypes.c_int64),
+                ("x_oriented", ctypes.c_int32), ("elem_bytes", ctypes.c_int32),
+                ("a_prime", ctypes.c_void_p), ("b_prime", ctypes.c_void_p), ("ld_m", ctypes.c_int64),
+                ("scalars", ctypes.c_void_p), ("m", ctypes.c_int32), ("n", ctypes.c_int32),
+                ("wide", ctypes.c_int32), ("reserved", ctypes.c_int32)]
 
 
 class AdamwTensor(ctypes.Structure):
@@ -98,6 +106,7 @@ def lib():
     L.dmuon_adamw_step_workspace_size.argtypes = [P(AdamwTensor), i32, P(sz)]
     L.dmuon_adamw_step.argtypes = [P(AdamwTensor), i32, P(AdamwCfg), vp, sz, vp]
     L.dmuon_gemm_nt.argtypes = [vp, vp, vp, i64, i64, i64, i64, i64, i64, i32, vp]
+    L.dmuon_debug_slice_buffers.argtypes = [P(Tensor), i32, P(StepCfg), vp, sz, i32, i64, P(DebugSlice)]
     L.dmuon_phase_timing.argtypes = [i32]
     L.dmuon_phase_timing_read.argtypes = [vp, vp, i32]
     L.dmuon_last_error.restype = ctypes.c_char_p

@@ -325,9 +325,9 @@ static int launch_plan(const Plan& pl, char* ws, int prec_f32, const LaunchScala
 // phase of the same tensors cannot start before it ends.  The tensors are
 // therefore split into work-balanced groups (greedy largest-first over an
 // estimate of each tensor's contraction work), each with its own table and
-// launch sequence; group 0 runs on the caller's stream and the others on
-// library streams forked from it and joined back with events, so one group's
-// tail rounds overlap another group's next phase.  Each slice's arithmetic is
+// launch sequence; group 0 runs on the caller's stream and the others on the
+// side streams the caller passes, forked from it and joined back with events,
+// so one group's tail rounds overlap another group's next phase.  Each slice's arithmetic is
 // the same whatever its group, so results do not depend on the split.
 // ---------------------------------------------------------------------------
 constexpr int kMaxGroups = 4;
@@ -673,7 +673,7 @@ using namespace dmuon;
 
 extern "C" {
 
-int32_t dmuon_abi_version(void) { return 4; }
+int32_t dmuon_abi_version(void) { return 5; }
 
 const char* dmuon_last_error(void) { return g_err.c_str(); }
 
@@ -745,6 +745,53 @@ int dmuon_muon_step(const dmuon_tensor* tensors, int32_t n, const dmuon_step_cfg
   if ((e = write_groups(gp, (char*)workspace, stream, fa))) return e;
   return launch_groups(gp, (char*)workspace, cfg->prec == DMUON_PREC_F32, step_scalars(cfg), cfg->ns_steps,
                        stream, side_streams, n_side_streams, fa);
+}
+
+int dmuon_debug_slice_buffers(const dmuon_tensor* tensors, int32_t n, const dmuon_step_cfg* cfg, void* workspace,
+                              size_t workspace_bytes, int32_t tensor, int64_t slice, dmuon_debug_slice* out) {
+  g_err.clear();
+  if (!out) return fail(DMUON_E_NULL, "out is NULL");
+  std::vector<Item> items;
+  GroupPlan gp;
+  int e = prepare_step(tensors, n, cfg, workspace, workspace_bytes, items, gp);
+  if (e) return e;
+  if (tensor < 0 || tensor >= n) return fail(DMUON_E_SHAPE, "tensor index out of range");
+  const dmuon_tensor& t = tensors[tensor];
+  const int64_t batch = t.ndim == 3 ? t.shape[0] : 1;
+  if (slice < 0 || slice >= batch) return fail(DMUON_E_SHAPE, "slice index out of range");
+  const bool f32 = cfg->prec == DMUON_PREC_F32;
+  const size_t esz = f32 ? 4 : 2;
+  // the momentum buffer is written, so no two tensors share it: it names the problem
+  for (size_t g = 0; g < gp.plans.size(); ++g) {
+    const Plan& pl = gp.plans[g];
+    for (const DevProblem& P : pl.probs) {
+      if (P.mom != t.momentum) continue;
+      dmuon_debug_slice d{};
+      const int64_t ld_s = P.wide ? P.ld_n : P.ld_m;
+      if (f32) {
+        d.x_copy = (const char*)P.xg + (size_t)(slice * P.m * P.ld_n) * esz;
+        d.x_rows = P.m;
+        d.x_ld = P.ld_n;
+        d.x_oriented = 1;
+      } else {
+        d.x_copy = (const char*)P.xs[0] + (size_t)(slice * P.rows * ld_s) * esz;
+        d.x_rows = P.rows;
+        d.x_ld = ld_s;
+        d.x_oriented = 0;
+      }
+      d.elem_bytes = (int32_t)esz;
+      d.a_prime = (const char*)P.ap + (size_t)(slice * P.m * P.ld_m) * esz;
+      d.b_prime = (const char*)P.bp + (size_t)(slice * P.m * P.ld_m) * esz;
+      d.ld_m = P.ld_m;
+      d.scalars = (const float*)((char*)workspace + gp.offs[g] + pl.off_scal) + (P.slice_base + slice) * kScalStride;
+      d.m = P.m;
+      d.n = P.n;
+      d.wide = P.wide;
+      *out = d;
+      return DMUON_OK;
+    }
+  }
+  return fail(DMUON_E_SHAPE, "the tensor has no slices (a zero-size dim)");
 }
 
 int dmuon_muon_step_noalloc(const dmuon_tensor* tensors, int32_t n, const dmuon_step_cfg* cfg, void* stream) {

@@ -32,7 +32,7 @@ def test_library_exports_every_header_function():
     for name in names:
         assert hasattr(L, name), name
     assert sorted(B.EXPORTED) == names
-    assert L.dmuon_abi_version() == 4 == B.ABI_VERSION
+    assert L.dmuon_abi_version() == 5 == B.ABI_VERSION
 
 
 # --------------------------------------------------------------------------
@@ -422,3 +422,60 @@ def test_adamw_forced_failure(monkeypatch, where):
     monkeypatch.setenv("DMUON_TEST_FAIL_AT", where)
     assert astep([adesc()]) == -8
     monkeypatch.delenv("DMUON_TEST_FAIL_AT")
+
+
+def test_debug_slice_buffers_layout():
+    """The per-phase test hook: host only, so it runs here on plausible
+    addresses.  Every buffer it reports lies inside the workspace, the
+    buffers of one slice do not overlap, consecutive slices sit one slice
+    stride apart, the shape fields follow the orientation rule, and bad
+    indices are rejected."""
+    L = B.lib()
+    descs = [desc(2, (300, 700), B.BF16, base=FAKE, numel_bytes=1 << 24),
+             desc(3, (3, 520, 300), B.F32, base=FAKE + (1 << 30), numel_bytes=1 << 24)]
+    arr = (B.Tensor * 2)(*descs)
+    for prec in ("bf16", "f32"):
+        for groups in (1, 2):
+            c = cfg(precision=prec, stream_groups=groups)
+            rc, need = wsize(descs, c)
+            assert rc == 0 and need > 0
+            ws = FAKE + (1 << 40)
+            esz = 2 if prec == "bf16" else 4
+
+            def get(t, s):
+                out = B.DebugSlice()
+                rc = L.dmuon_debug_slice_buffers(arr, 2, ctypes.byref(c), ctypes.c_void_p(ws), need, t, s,
+                                                 ctypes.byref(out))
+                return rc, out
+
+            rc, d0 = get(0, 0)
+            assert rc == 0
+            assert (d0.m, d0.n, d0.wide, d0.elem_bytes) == (300, 700, 1, esz)
+            assert d0.ld_m == 320
+            rc, d1 = get(1, 1)
+            rc2, d2 = get(1, 2)
+            assert rc == 0 and rc2 == 0
+            assert (d1.m, d1.n, d1.wide) == (300, 520, 0)
+            if prec == "bf16":      # the tensor's own layout (tall: 520 rows of 300)
+                assert (d0.x_rows, d0.x_oriented, d1.x_rows, d1.x_oriented) == (300, 0, 520, 0)
+                assert d0.x_ld >= 700 and d0.x_ld % 64 == 0 and d1.x_ld >= 300 and d1.x_ld % 64 == 0
+            else:                   # oriented X: m rows of n
+                assert (d0.x_rows, d0.x_oriented, d1.x_rows, d1.x_oriented) == (300, 1, 300, 1)
+                assert d0.x_ld >= 700 and d1.x_ld >= 520
+            for d in (d0, d1, d2):
+                regions = [(d.x_copy, d.x_rows * d.x_ld * esz), (d.a_prime, d.m * d.ld_m * esz),
+                           (d.b_prime, d.m * d.ld_m * esz), (d.scalars, 4 * 8)]
+                for lo, size in regions:
+                    assert ws <= lo and lo + size <= ws + need
+                regions.sort()
+                for (lo, size), (lo2, _) in zip(regions, regions[1:]):
+                    assert lo + size <= lo2
+            assert d2.a_prime - d1.a_prime == d1.m * d1.ld_m * esz
+            assert d2.x_copy - d1.x_copy == d1.x_rows * d1.x_ld * esz
+            assert d2.scalars - d1.scalars == 80 * 4
+            assert get(2, 0)[0] == -3 and get(1, 3)[0] == -3 and get(0, 1)[0] == -3 and get(-1, 0)[0] == -3
+            rc = L.dmuon_debug_slice_buffers(arr, 2, ctypes.byref(c), ctypes.c_void_p(ws), need, 0, 0, None)
+            assert rc == -1
+            rc = L.dmuon_debug_slice_buffers(arr, 2, ctypes.byref(c), ctypes.c_void_p(ws), need - 256, 0, 0,
+                                             ctypes.byref(B.DebugSlice()))
+            assert rc == -6
