@@ -332,6 +332,18 @@ def test_many_slices_and_many_tensors(precision):
                 "1200 tensors")
 
 
+@pytest.mark.parametrize("precision", ["bf16", "f32"])
+def test_step_extreme_gradient_scales(precision):
+    """The bf16 path's first Gram multiplies the unscaled copy of B and applies
+    inv² after the fp32 sums, so those sums see |B|²: gradients 1e-12 and 1e9
+    in magnitude (B = G, zero momentum) stay within the oracle's bounds; at
+    1e-12 eps dominates the norm, as it does in the oracle."""
+    for scale in (1e-12, 1e9):
+        tds = [make_custom((300, 700), "f32", seed=(80, 0), scale=scale, nonzero_momentum=False),
+               make_custom((700, 300), "bf16", seed=(80, 1), scale=scale, nonzero_momentum=False)]
+        check_step(tds, precision, label=f"gradient scale {scale:g}")
+
+
 def test_step_zero_gradient():
     td = make_custom((300, 500), "f32", seed=(63, 0), nonzero_momentum=False)
     td.grad[:] = 0
