@@ -191,6 +191,23 @@ def select_share(wl_name):
     return wl, [int(i) for i in res["owner_order"]]
 
 
+def lpt_summary(wl_name):
+    """The LPT partition behind a workload's owner share (None when it is stepped
+    whole): slot count, the owner's slot and matrix count, every slot's load in
+    elements and the max/mean balance."""
+    if wl_name != "llama_d4096":
+        return None
+    from matrix_optimizer_muon_amd import lpt_assign
+    from matrix_optimizer_muon_amd.workloads import workload
+    wl = workload(wl_name)
+    rows = [t.shape[0] for t in wl.tensors]
+    cols = [t.shape[1] for t in wl.tensors]
+    res = lpt_assign(rows, cols, [1] * len(rows), [t.layer for t in wl.tensors], 8, owner_slot=0)
+    loads = [int(v) for v in res["slot_load"]]
+    return {"slots": 8, "owner_slot": 0, "owned_matrices": int(len(res["owner_order"])),
+            "slot_loads_elements": loads, "max_over_mean": round(max(loads) * len(loads) / sum(loads), 4)}
+
+
 def blas_threads():
     try:
         from threadpoolctl import threadpool_info
@@ -524,7 +541,8 @@ def main():
         "config": {"workload": args.workload, "matrices": slices, "shapes": shapes,
                    "stream_groups": groups_used, "graph": bool(args.graph),
                    "ns_steps": HYPER["steps"], "grad_dtype": ts[0].grad_dtype,
-                   "effective_gflop_per_step": round(flops / 1e9, 1), "publish": bool(args.publish)},
+                   "effective_gflop_per_step": round(flops / 1e9, 1), "publish": bool(args.publish),
+                   "lpt": lpt_summary(args.workload)},
         "roofline": roof,
         "cpu_baseline": cpu,
         "elementwise": elementwise,

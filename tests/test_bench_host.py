@@ -77,3 +77,15 @@ def test_more_than_one_gpu_is_refused():
                        capture_output=True, text=True, timeout=300)
     assert r.returncode == 2
     assert "one GPU" in (r.stdout + r.stderr)
+
+
+def test_lpt_summary_of_the_llama_share():
+    """The bench line's partition summary: 8 slots whose loads add up to the
+    whole 32-layer model, slot 0 owning 29 matrices, max/mean 1.0207; none for
+    a workload stepped whole."""
+    s = bench.lpt_summary("llama_d4096")
+    model = 32 * (4 * 4096 * 4096 + 3 * 4096 * 11008)
+    assert s["slots"] == 8 and s["owner_slot"] == 0 and s["owned_matrices"] == 29
+    assert sum(s["slot_loads_elements"]) == model
+    assert s["max_over_mean"] == 1.0207
+    assert bench.lpt_summary("mlp_moe_large") is None
