@@ -89,6 +89,27 @@ def measured_traffic(kernel, workload_name):
         return None
 
 
+def measured_mfma_busy(workload_name):
+    """Per-kernel matrix-core busy share and clock from the committed rocprofv3
+    counter summary (GRBM_GUI_ACTIVE, SQ_VALU_MFMA_BUSY_CYCLES), or None when the
+    summary is missing or was taken on other kernel sources."""
+    path = os.path.join(PROFILES, f"mfma_busy_{workload_name}.md")
+    if not os.path.exists(path):
+        return None
+    out, sha = {}, None
+    with open(path) as f:
+        for line in f:
+            if line.strip().startswith("- kernels_sha256:"):
+                sha = line.split(":", 1)[1].strip().strip("`")
+            cells = [c.strip() for c in line.strip().strip("|").split("|")]
+            if len(cells) == 6 and cells[3].replace(".", "", 1).isdigit() and cells[4].endswith("%"):
+                out[cells[0].replace("\u2212", "-")] = {"clock_ghz": float(cells[3]),
+                                                        "mfma_busy": round(float(cells[4][:-1]) / 100, 4)}
+    if sha != kernels_sha256() or not out:
+        return None
+    return {"source": os.path.relpath(path, ROOT), "kernels": out}
+
+
 def peak_clock_mhz(device_index):
     """The device's peak shader clock (hipDeviceGetAttribute with
     hipDeviceAttributeClockRate, value 5 in ROCm 7's hip_runtime_api.h, in kHz),
@@ -544,6 +565,7 @@ def main():
                    "effective_gflop_per_step": round(flops / 1e9, 1), "publish": bool(args.publish),
                    "lpt": lpt_summary(args.workload)},
         "roofline": roof,
+        "counters": measured_mfma_busy(args.workload),
         "cpu_baseline": cpu,
         "elementwise": elementwise,
         "phases_ms_per_step": {k: round(v[0] / args.steps, 4) for k, v in phases.items() if v[1]},

@@ -89,3 +89,21 @@ def test_lpt_summary_of_the_llama_share():
     assert sum(s["slot_loads_elements"]) == model
     assert s["max_over_mean"] == 1.0207
     assert bench.lpt_summary("mlp_moe_large") is None
+
+
+def test_measured_mfma_busy_lookup(tmp_path, monkeypatch):
+    """The counter summary behind the line's `counters`: read only while it was
+    taken on the current kernel sources; the committed headline one parses."""
+    got = bench.measured_mfma_busy("mlp_moe_large")
+    if got is not None:                   # the committed summary matches these sources
+        assert {"gram", "square", "apply (0 < t < k-1)"} <= set(got["kernels"])
+        assert all(0 <= v["mfma_busy"] <= 1 and 0.5 < v["clock_ghz"] < 2.5 for v in got["kernels"].values())
+    monkeypatch.setattr(bench, "PROFILES", str(tmp_path))
+    assert bench.measured_mfma_busy("layer_d2048") is None
+    f = tmp_path / "mfma_busy_layer_d2048.md"
+    table = ("| kernel | dispatches | average (us) | clock (GHz) | MFMA busy | MFMA instructions / dispatch |\n"
+             "|---|---|---|---|---|---|\n| gram | 15 | 100.0 | 1.75 | 64.5% | 1.1e+08 |\n")
+    f.write_text(f"# x\n\n- kernels_sha256: `{bench.kernels_sha256()}`\n\n{table}")
+    assert bench.measured_mfma_busy("layer_d2048")["kernels"] == {"gram": {"clock_ghz": 1.75, "mfma_busy": 0.645}}
+    f.write_text(f"# x\n\n- kernels_sha256: `0000`\n\n{table}")
+    assert bench.measured_mfma_busy("layer_d2048") is None
