@@ -64,3 +64,50 @@ def test_noalloc_matches_the_workspace_step(precision):
             assert rel(O, Oo) <= TOL[precision]
             assert rel(g[1].cpu().numpy(), Bo) <= 1e-6
             assert rel(g[2].cpu().numpy(), oracle.decay_update(td.master, O, HYPER["lr"], HYPER["wd"])) <= 1e-6
+
+
+@pytest.mark.parametrize("precision", ["bf16", "f32"])
+def test_noalloc_captured_in_a_graph(precision):
+    """Code under graph capture is one of the callers the allocation-free step
+    is for: the step captured into a graph (its table copies are kernels, so
+    every replay rewrites the scratch tables) and replayed twice, with eager
+    work and synchronisations between the replays, gives the bits of two
+    direct allocation-free steps."""
+    tds = [make_custom((600, 1000), "bf16", seed=(92, 0), scale=1e-3),
+           make_custom((2, 520, 300), "f32", seed=(92, 1))]
+
+    def setup():
+        devs = [to_dev(td) for td in tds]
+        cfg = B.make_cfg(HYPER["lr"], HYPER["mu"], HYPER["wd"], HYPER["eps"], Q5, HYPER["steps"], precision)
+        arr, n = B.make_descs([d[0] for d in devs], [d[1] for d in devs], [d[2] for d in devs],
+                              [d[3] for d in devs])
+        return devs, cfg, arr, n
+
+    def call(cfg, arr, n):
+        B.check(B.lib().dmuon_muon_step_noalloc(arr, n, ctypes.byref(cfg),
+                                                ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)))
+
+    def snap(devs):
+        return [[d[k].cpu().numpy() for k in (1, 2, 3)] for d in devs]
+
+    devs, cfg, arr, n = setup()
+    call(cfg, arr, n)
+    torch.cuda.synchronize()
+    want1 = snap(devs)
+    call(cfg, arr, n)
+    torch.cuda.synchronize()
+    want2 = snap(devs)
+
+    devs, cfg, arr, n = setup()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        call(cfg, arr, n)
+    torch.cuda.synchronize()
+    for want in (want1, want2):
+        graph.replay()
+        torch.cuda.synchronize()
+        junk = torch.randn(1 << 20, device="cuda") * 2.0       # eager work between the replays
+        torch.cuda.synchronize()
+        del junk
+        for w, g in zip(want, snap(devs)):
+            assert all(np.array_equal(a, b) for a, b in zip(w, g))
