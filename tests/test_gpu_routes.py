@@ -231,3 +231,45 @@ def test_adamw_workloads_full(name):
     wl = workload(name)
     ads = [make_adamw(wl, t) for t in wl.tensors]
     check_adamw(ads, 10)
+
+
+def test_prepared_steps_in_a_training_loop():
+    """The prepared Muon step (2-D weights) and AdamW step (1-D biases) driving
+    a small bf16 MLP as a training loop would: gradients kept in place between
+    iterations (zero_grad(set_to_none=False)), fp32 masters and state in
+    caller tensors, the bf16 weights rewritten by the steps' published copies.
+    After each iteration every bf16 weight is the round-to-nearest-even bf16 of
+    its fp32 master, and the loss stays finite."""
+    import matrix_optimizer_muon_amd as mm
+    torch.manual_seed(0)
+    model = torch.nn.Sequential(torch.nn.Linear(64, 300), torch.nn.ReLU(),
+                                torch.nn.Linear(300, 40)).cuda().to(torch.bfloat16)
+    x = torch.randn(256, 64, device="cuda").to(torch.bfloat16)
+    y = torch.randn(256, 40, device="cuda")
+
+    def backward():
+        loss = torch.nn.functional.mse_loss(model(x).float(), y)
+        loss.backward()
+        return float(loss.detach())
+
+    mats = [p for p in model.parameters() if p.dim() >= 2]
+    vecs = [p for p in model.parameters() if p.dim() < 2]
+    masters = [p.detach().float() for p in mats]
+    momenta = [torch.zeros_like(w) for w in masters]
+    v_master = [p.detach().float() for p in vecs]
+    m1, m2 = [torch.zeros_like(w) for w in v_master], [torch.zeros_like(w) for w in v_master]
+    start = [w.clone() for w in masters]
+    backward()
+    muon = mm.MuonStep([p.grad for p in mats], momenta, masters, lr=0.02, momentum=0.95,
+                       weight_decay=0.01, param_outs=[p.data for p in mats])
+    adamw = mm.AdamwStep(v_master, [p.grad for p in vecs], m1, m2, lr=1e-3, param_outs=[p.data for p in vecs])
+    for it in range(1, 4):
+        muon()
+        adamw(it)
+        torch.cuda.synchronize()
+        for p, w in list(zip(mats, masters)) + list(zip(vecs, v_master)):
+            assert torch.equal(p.data, w.to(torch.bfloat16)), (it, tuple(p.shape))
+        model.zero_grad(set_to_none=False)
+        loss = backward()
+        assert np.isfinite(loss), it
+    assert all(not torch.equal(a, b) for a, b in zip(start, masters))
