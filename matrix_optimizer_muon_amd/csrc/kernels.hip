@@ -456,6 +456,9 @@ __global__ __launch_bounds__(kThreads) void k_adamw(AdamwTable tab, AdamwScalars
 // beyond it is dropped, which replaces per-element predicates (and the branches
 // they would need) in the apply epilogue.
 constexpr unsigned kOob = 0x7ffffff0u;       // an offset beyond every range used here
+// Word 3 of a buffer descriptor: data format 32 (bits 15–18 = 4), which raw
+// (untyped) buffer accesses need to be non-zero; no swizzle, no index stride.
+constexpr int kRsrcFlags = 0x00020000;
 // The fields are workgroup-uniform; readfirstlane tells the compiler so (a
 // descriptor it cannot prove uniform is rebuilt per lane in a loop).
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t range_rsrc(const void* p, int64_t bytes) {
@@ -463,7 +466,7 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t range_rsrc(const void* p, int6
   const unsigned lo = __builtin_amdgcn_readfirstlane((unsigned)a);
   const unsigned hi = __builtin_amdgcn_readfirstlane((unsigned)(a >> 32));
   const int n = __builtin_amdgcn_readfirstlane(p ? (int)bytes : 0);
-  return __builtin_amdgcn_make_buffer_rsrc((void*)(((uint64_t)hi << 32) | lo), 0, n, 0x00020000);
+  return __builtin_amdgcn_make_buffer_rsrc((void*)(((uint64_t)hi << 32) | lo), 0, n, kRsrcFlags);
 }
 __device__ __forceinline__ float buf_ld(__amdgpu_buffer_rsrc_t r, unsigned off) {
   return __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(r, (int)off, 0, 0));
@@ -581,9 +584,9 @@ __device__ __forceinline__ void gemm_mainloop(const Operands& op, char* smem, f3
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);    // wave-uniform
   const int wr = wave >> 2, wc = wave & 3, h = lane >> 5, r32 = lane & 31;
   const __amdgpu_buffer_rsrc_t ra = __builtin_amdgcn_make_buffer_rsrc(
-      (void*)op.a, 0, (op.rows_a < kTile ? op.rows_a : kTile) * op.lda_b, 0x00020000);
+      (void*)op.a, 0, (op.rows_a < kTile ? op.rows_a : kTile) * op.lda_b, kRsrcFlags);
   const __amdgpu_buffer_rsrc_t rb = __builtin_amdgcn_make_buffer_rsrc(
-      (void*)op.b, 0, (op.rows_b < kTile ? op.rows_b : kTile) * op.ldb_b, 0x00020000);
+      (void*)op.b, 0, (op.rows_b < kTile ? op.rows_b : kTile) * op.ldb_b, kRsrcFlags);
   // DMA: wave w fills rows [32w, 32w + 32) of A and of B, 16 rows per instruction;
   // lane l lands at byte 16·l of the instruction's 1 KiB = row l/4, physical chunk l%4.
   // K-major: the instruction's 1 KiB is k-rows 2(2w + q) and 2(2w + q) + 1; lane l
