@@ -28,6 +28,7 @@
 // operand row-major.
 #include <hip/hip_runtime.h>
 
+#include <atomic>
 #include <cstdint>
 #include <mutex>
 #include <type_traits>
@@ -1657,12 +1658,20 @@ static int set_lds(K kernel) {
   return (int)hipFuncSetAttribute((const void*)kernel, hipFuncAttributeMaxDynamicSharedMemorySize, kGemmLds);
 }
 
-static int lds_ready_bf16 = 0, lds_ready_f32 = 0;
+// The contraction kernels' dynamic-LDS limit is raised once per device and
+// precision (the attribute belongs to the device's copy of the kernel); first
+// calls may come from several threads, hence the atomic bit set and the lock.
+static std::atomic<uint64_t> g_lds_ready{0};
+static std::mutex g_lds_mu;
 
 static int ensure_lds(int f32) {
-  int& flag = f32 ? lds_ready_f32 : lds_ready_bf16;
-  if (flag) return 0;
-  int e = 0;
+  int dev = 0;
+  int e = (int)hipGetDevice(&dev);
+  if (e) return e;
+  const uint64_t bit = dev >= 0 && dev < 32 ? (uint64_t)1 << (2 * dev + (f32 ? 1 : 0)) : 0;
+  if (bit && (g_lds_ready.load(std::memory_order_acquire) & bit)) return 0;
+  std::lock_guard<std::mutex> lk(g_lds_mu);
+  if (bit && (g_lds_ready.load(std::memory_order_relaxed) & bit)) return 0;
   if (f32) {
     e |= set_lds(k_gemm<float, PH_GRAM, false>);
     e |= set_lds(k_gemm<float, PH_SQUARE, false>);
@@ -1680,7 +1689,7 @@ static int ensure_lds(int f32) {
     e |= set_lds(k_gemm<uint16_t, PH_APPLY, true, true>);
     e |= set_lds(k_gemm_plain<uint16_t>);
   }
-  if (e == 0) flag = 1;
+  if (e == 0 && bit) g_lds_ready.fetch_or(bit, std::memory_order_release);
   return e;
 }
 
