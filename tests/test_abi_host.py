@@ -479,3 +479,42 @@ def test_debug_slice_buffers_layout():
             rc = L.dmuon_debug_slice_buffers(arr, 2, ctypes.byref(c), ctypes.c_void_p(ws), need - 256, 0, 0,
                                              ctypes.byref(B.DebugSlice()))
             assert rc == -6
+
+
+def test_workspace_regions_of_all_slices_are_disjoint():
+    """The planner's workspace layout, on 30 seeded random tensor sets (2-D and
+    3-D, wide and tall, ragged, both precisions, 1–4 groups): every slice's
+    operand copy, A′, B′ and scalars lie inside the workspace, and no two of
+    these regions, of the same or of different slices and tensors, overlap."""
+    L = B.lib()
+    rng = np.random.default_rng(12345)
+    for case in range(30):
+        n = int(rng.integers(1, 6))
+        descs = []
+        for k in range(n):
+            rows, cols = int(rng.integers(1, 1500)), int(rng.integers(1, 1500))
+            ndim = 3 if rng.random() < 0.4 else 2
+            batch = int(rng.integers(1, 4))
+            shape = (batch, rows, cols) if ndim == 3 else (rows, cols)
+            descs.append(desc(ndim, shape, B.BF16 if rng.random() < 0.5 else B.F32,
+                              base=FAKE + k * (1 << 32), numel_bytes=1 << 30))
+        prec = "bf16" if rng.random() < 0.5 else "f32"
+        c = cfg(precision=prec, stream_groups=int(rng.integers(1, 5)))
+        rc, need = wsize(descs, c)
+        assert rc == 0 and need > 0
+        ws = FAKE + (1 << 44)
+        esz = 2 if prec == "bf16" else 4
+        arr = (B.Tensor * n)(*descs)
+        regions = []
+        for t, dsc in enumerate(descs):
+            for s in range(dsc.shape[0] if dsc.ndim == 3 else 1):
+                d = B.DebugSlice()
+                assert L.dmuon_debug_slice_buffers(arr, n, ctypes.byref(c), ctypes.c_void_p(ws), need, t, s,
+                                                   ctypes.byref(d)) == 0
+                regions += [(d.x_copy, d.x_rows * d.x_ld * esz), (d.a_prime, d.m * d.ld_m * esz),
+                            (d.b_prime, d.m * d.ld_m * esz), (d.scalars, 80 * 4)]
+        regions.sort()
+        for lo, size in regions:
+            assert ws <= lo and lo + size <= ws + need, case
+        for (lo, size), (lo2, _) in zip(regions, regions[1:]):
+            assert lo + size <= lo2, case
