@@ -37,3 +37,19 @@ def test_bench_line(graph):
     assert abs(roof["frac"] - roof["achieved"] / roof["peak"]) < 1e-3
     assert line["device"]["cus"] > 0 and line["device"]["peak_clock_mhz"] > 0
     print(f"graph={graph}: {line['ms_per_step']} ms per step on {line['device']}", flush=True)
+
+
+def test_bench_adamw_route_line():
+    """The adamw route's line on the 65 RMSNorm vectors: elements per second,
+    an HBM roofline whose fraction is achieved / 8 TB/s."""
+    cmd = [sys.executable, os.path.join(ROOT, "bench.py"), "--route", "adamw", "--workload", "adamw_llama_norms",
+           "--steps", "20", "--warmup", "3", "--no-cpu-baseline"]
+    print("running:", " ".join(cmd), flush=True)
+    r = subprocess.run(cmd, capture_output=True, text=True, timeout=240, cwd=ROOT)
+    assert r.returncode == 0, r.stderr[-2000:]
+    line = json.loads(r.stdout.strip().splitlines()[-1])
+    assert line["unit"] == "elements/s" and line["value"] > 0 and line["n_gpus"] == 1
+    assert line["config"]["workload"] == "adamw_llama_norms"
+    roof = line["roofline"]
+    assert roof["bound"] == "hbm" and roof["unit"] == "GB/s" and roof["peak"] == 8000.0
+    assert abs(roof["frac"] - roof["achieved"] / roof["peak"]) < 1e-3
