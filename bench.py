@@ -25,6 +25,13 @@ pass (``--stream-groups 1`` makes both passes alike, which is the configuration
 the committed rocprofv3 kernel summaries are taken on).  ``--publish`` also writes the
 bf16 published copy of every updated master inside the step.
 
+After the two passes the line's ``mfma_ceiling`` times the probe library's
+matrix-core-only waves (v_mfma_f32_32x32x16_bf16 on random register operands,
+the contraction kernels' instruction) for 3 s under the same board power
+limit; ``roofline.frac_of_mfma_ceiling`` is the dominant kernel's rate over
+that ceiling.  ``--mfma-probe`` prints the ceiling of both instruction shapes on
+random and zero operands.
+
 ``--graph`` captures the prepared step of the first pass into a HIP graph and
 times its replays instead (one graph launch per step), which shows what the
 launches themselves cost on small workloads.
@@ -135,6 +142,71 @@ def copy_probe(nbytes):
         dst.copy_(src)
     torch.cuda.synchronize()
     print(json.dumps({"copy_probe_bytes": nbytes}), flush=True)
+
+
+def mfma_ceiling(shape=32, operands=0, seconds=3.0, settle=1.0):
+    """What the matrix cores sustain on their own: the probe library's waves issue
+    only bf16 MFMAs (32×32×16 or 16×16×32) on register operands, back to back,
+    for ``settle`` seconds and then ``seconds`` timed with HIP events on the
+    launch stream, while a thread samples the board power and shader clock the
+    driver reports (torch.cuda.power_draw / clock_rate, amd-smi's readings).
+    With random operands this is the ceiling the board's power limit sets; with
+    zero operands (operands=1) it is the unloaded bound."""
+    import threading
+    import torch
+    from matrix_optimizer_muon_amd import probe
+
+    blocks, iters = 2048, 20000
+    sink = torch.empty(blocks * probe.THREADS, dtype=torch.float32, device="cuda")
+    st = torch.cuda.current_stream()
+    launch = lambda: probe.probe_mfma(shape, operands, blocks, iters, sink.data_ptr(), st.cuda_stream)
+    t_end = time.perf_counter() + settle
+    while time.perf_counter() < t_end:
+        launch()
+        torch.cuda.synchronize()
+    samples, stop = [], threading.Event()
+
+    def sample():
+        while not stop.is_set():
+            try:
+                samples.append((float(torch.cuda.power_draw()), float(torch.cuda.clock_rate())))
+            except Exception:
+                return
+            time.sleep(0.05)
+
+    th = threading.Thread(target=sample)
+    th.start()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    n = 0
+    ev0.record(st)
+    t_end = time.perf_counter() + seconds
+    while time.perf_counter() < t_end:
+        for _ in range(4):
+            launch()
+        n += 4
+        torch.cuda.synchronize()
+    ev1.record(st)
+    torch.cuda.synchronize()
+    stop.set()
+    th.join()
+    ms = ev0.elapsed_time(ev1) / n
+    tflops = probe.flops_per_launch(blocks, iters) / (ms * 1e-3) / 1e12
+    out = {"instruction": f"v_mfma_f32_{shape}x{shape}x{512 // shape}_bf16",
+           "operands": "random bf16" if operands == 0 else "zero",
+           "tflops": round(tflops, 1), "frac_of_peak": round(tflops / PEAK_BF16_TFLOPS, 4),
+           "launches": n, "ms_per_launch": round(ms, 3), "power_w": None, "clock_mhz": None}
+    if samples:
+        out["power_w"] = round(sum(p for p, _ in samples) / len(samples), 1)
+        out["clock_mhz"] = round(sum(c for _, c in samples) / len(samples), 1)
+    return out
+
+
+def mfma_probe():
+    """--mfma-probe: the matrix-core ceiling for both instruction shapes, random
+    and zero operands, one JSON line each."""
+    for shape in (32, 16):
+        for operands in (0, 1):
+            print(json.dumps(mfma_ceiling(shape, operands)), flush=True)
 
 
 def copy_ceiling_gbs(nbytes=1 << 30, reps=10):
@@ -427,11 +499,18 @@ def main():
                     help="concurrent stream groups of the value pass (0: the library's choice)")
     ap.add_argument("--graph", action="store_true",
                     help="value pass: capture one prepared step into a HIP graph and time its replays")
+    ap.add_argument("--mfma-probe", action="store_true",
+                    help="only measure the matrix-core ceiling (probe library), both shapes")
+    ap.add_argument("--no-mfma-ceiling", action="store_true",
+                    help="skip the 3 s matrix-core ceiling measurement of the main line")
     ap.add_argument("--copy-probe", type=int, default=0,
                     help="only run a plain device copy of this many bytes (counter calibration)")
     args = ap.parse_args()
     if args.copy_probe:
         copy_probe(args.copy_probe)
+        return
+    if args.mfma_probe:
+        mfma_probe()
         return
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -541,6 +620,13 @@ def main():
                        "target_frac": 0.8,
                        "note": "the decay + update runs inside the last apply launch (no separate kernel)"}
 
+    # the matrix cores alone on the dominant kernel's instruction, under the same
+    # power limit: the practical ceiling of a bf16 contraction on random operands
+    ceiling = None
+    if roof and args.precision == "bf16" and not args.no_mfma_ceiling:
+        ceiling = mfma_ceiling(32, 0)
+        roof["frac_of_mfma_ceiling"] = round(roof["achieved"] / ceiling["tflops"], 4)
+
     cpu = None
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(wl, ts)
@@ -568,6 +654,7 @@ def main():
         "counters": measured_mfma_busy(args.workload),
         "cpu_baseline": cpu,
         "elementwise": elementwise,
+        "mfma_ceiling": ceiling,
         "phases_ms_per_step": {k: round(v[0] / args.steps, 4) for k, v in phases.items() if v[1]},
         # one-stream pass: Newton–Schulz contractions alone, element-wise kernels alone
         "ns_ms_per_step": round(sum(phases[p][0] for p in ("gram", "square", "apply") if p in phases)
