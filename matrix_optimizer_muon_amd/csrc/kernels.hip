@@ -32,6 +32,7 @@
 #include <cstdint>
 #include <mutex>
 #include <type_traits>
+#include <utility>
 #include <vector>
 
 #include "internal.hpp"
@@ -533,8 +534,12 @@ struct Operands {
   int ktiles;        // stages: K elements / 32 (bf16) or / 16 (fp32)
 };
 
-// K-major stage layout: 32-byte segment s of k-row r sits at segment s ^ kmaj_swz(r)
-__device__ __forceinline__ int kmaj_swz(int r) { return 2 * (r & 3); }
+// K-major stage layout: 32-byte segment s of k-row r sits at segment s ^ kmaj_swz(r).
+// A transposing fragment read has 16-lane groups read four consecutive k-rows of
+// one 16-column segment, the two groups of a half-wave k-rows 8 apart: bits 0-1
+// of r spread a group's rows over four segment pairs and bit 3 moves the other
+// group's rows to the odd segments, so a half-wave touches 8 distinct segments.
+__device__ __forceinline__ int kmaj_swz(int r) { return (2 * (r & 3)) ^ ((r >> 3) & 1); }
 
 template <typename T>
 __device__ __forceinline__ void mfma_chunk(f32x16_t& acc, const u32x4_t& a, const u32x4_t& b);
@@ -545,6 +550,55 @@ __device__ __forceinline__ void mfma_chunk<uint16_t>(f32x16_t& acc, const u32x4_
   __builtin_memcpy(&va, &a, 16);
   __builtin_memcpy(&vb, &b, 16);
   acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, vb, acc, 0, 0, 0);
+}
+
+// f(std::integral_constant<int, 0>{}) … f(std::integral_constant<int, N − 1>{})
+template <typename F, int... I>
+__device__ __forceinline__ void static_for_seq(F&& f, std::integer_sequence<int, I...>) {
+  (f(std::integral_constant<int, I>{}), ...);
+}
+template <int N, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+  static_for_seq(f, std::make_integer_sequence<int, N>{});
+}
+
+// bf16 contraction step on one 16×16 quarter of a 32×32 accumulator block.
+// During the K loop quarter (R, C) (rows 16R.., columns 16C.. of the block) lives
+// in registers 4(2R + C) .. 4(2R + C) + 3 in the 16×16×32 output layout: lane l,
+// register i holds row 4(l >> 4) + i, column l & 15.  The operands: lane l holds
+// row (A) or column (B) l & 15 and k = 8(l >> 4) .. 8(l >> 4) + 7 of the 32-deep
+// stage.  quarters_to_32x32 turns the block into the 32×32×16 output layout the
+// epilogues read (acc_row / acc_col).
+template <int Q>
+__device__ __forceinline__ void mfma_quarter(f32x16_t& acc, const u32x4_t& a, const u32x4_t& b) {
+  bf16x8_t va, vb;
+  __builtin_memcpy(&va, &a, 16);
+  __builtin_memcpy(&vb, &b, 16);
+  f32x4_t q = {acc[4 * Q], acc[4 * Q + 1], acc[4 * Q + 2], acc[4 * Q + 3]};
+  q = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, vb, q, 0, 0, 0);
+  acc[4 * Q] = q[0];
+  acc[4 * Q + 1] = q[1];
+  acc[4 * Q + 2] = q[2];
+  acc[4 * Q + 3] = q[3];
+}
+
+// Quarter layout → 32×32×16 layout, in place.  In the 32×32 layout lane l,
+// register 4g + i holds row 8g + 4(l >> 5) + i, column l & 31; that value sits in
+// quarter (g >> 1, (l >> 4) & 1) at lane 32(g & 1) + 16(l >> 5) + (l & 15),
+// register i.  Per register pair (quarters (R, 0) and (R, 1)) this is a swap of
+// lane bit 4 with the pair index followed by a swap of lane bit 5 with it:
+// v_permlane16_swap then v_permlane32_swap.
+__device__ __forceinline__ void quarters_to_32x32(f32x16_t& acc) {
+#pragma unroll
+  for (int R = 0; R < 2; ++R)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const auto s16 = __builtin_amdgcn_permlane16_swap(__float_as_uint(acc[8 * R + i]),
+                                                        __float_as_uint(acc[8 * R + 4 + i]), false, false);
+      const auto s32 = __builtin_amdgcn_permlane32_swap(s16[0], s16[1], false, false);
+      acc[8 * R + i] = __uint_as_float(s32[0]);
+      acc[8 * R + 4 + i] = __uint_as_float(s32[1]);
+    }
 }
 
 // fp32: a 16-byte chunk holds 4 consecutive k; element e of the two lane halves
@@ -602,44 +656,50 @@ __device__ __forceinline__ void gemm_mainloop(const Operands& op, char* smem, f3
     offa[q] = TA ? kr * op.lda_b + op.cola_b + lun * 16 : row * op.lda_b + c * 16;
     offb[q] = TB ? kr * op.ldb_b + op.colb_b + lun * 16 : row * op.ldb_b + c * 16;
   }
-  // fragment offsets inside a stage for logical chunk 2·ss + h
+  // Fragments of one stage.  bf16 (16×16×32 quarters): fa[ss][i] is rows
+  // 16(4ss + i) .. +15 of the wave's 128 and fb[ss][j] columns 16(2ss + j) .. +15
+  // of its 64, all 32 k, lane l reading logical chunk l >> 4 of row l & 15.
+  // fp32 (32×32×2): fa[ss][i] / fb[ss][j] are 32-row / 32-column blocks i / j and
+  // 16-k chunk ss, lane l reading logical chunk 2·ss + (l >> 5) of row l & 31.
+  constexpr bool kQ = sizeof(T) == 2;
   int fa_off[2][4], fb_off[2][2];
 #pragma unroll
   for (int ss = 0; ss < 2; ++ss) {
-    const int c = 2 * ss + h;
+    const int c = kQ ? lane >> 4 : 2 * ss + h;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const int row = wr * 128 + i * 32 + r32;
+      const int row = kQ ? wr * 128 + 16 * (4 * ss + i) + (lane & 15) : wr * 128 + i * 32 + r32;
       fa_off[ss][i] = row * kRowBytes + ((c ^ ((row >> 2) & 3)) * 16);
     }
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
-      const int row = wc * 64 + j * 32 + r32;
+      const int row = kQ ? wc * 64 + 16 * (2 * ss + j) + (lane & 15) : wc * 64 + j * 32 + r32;
       fb_off[ss][j] = kTile * kRowBytes + row * kRowBytes + ((c ^ ((row >> 2) & 3)) * 16);
     }
   }
-  // K-major fragments: two transposing 8-byte reads (k 0..3 and 4..7 of the
-  // lane's 8-k block); in each 16-lane group, source lane i reads k-row i >> 2,
-  // columns 4(i & 3) .. +3 of the group's 16 columns, and lane i receives column
-  // i of the group, four consecutive k
+  // K-major fragments (bf16, quarter layout): two transposing 8-byte reads (k
+  // 0..3 and 4..7 of the lane's 8-k block 8(l >> 4)); in each 16-lane group,
+  // source lane i reads k-row 8(l >> 4) + 4t + (i >> 2), columns 4(i & 3) .. +3 of
+  // the quarter's 16 columns, and lane i receives column i of the quarter, four
+  // consecutive k
   int ta_off[TA ? 2 : 1][4][2], tb_off[TB ? 2 : 1][2][2];
 #pragma unroll
   for (int ss = 0; ss < 2; ++ss)
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
-      const int kr = 16 * ss + 8 * h + 4 * t + ((lane & 15) >> 2);
-      const int sub = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
+      const int kr = 8 * (lane >> 4) + 4 * t + ((lane & 15) >> 2);
+      const int sub = 4 * (lane & 3);
       if (TA) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          const int n = wr * 128 + i * 32 + sub;
+          const int n = wr * 128 + 16 * (4 * ss + i) + sub;
           ta_off[TA ? ss : 0][i][t] = kr * 512 + (((n >> 4) ^ kmaj_swz(kr)) << 5) + ((2 * n) & 31);
         }
       }
       if (TB) {
 #pragma unroll
         for (int j = 0; j < 2; ++j) {
-          const int n = wc * 64 + j * 32 + sub;
+          const int n = wc * 64 + 16 * (2 * ss + j) + sub;
           tb_off[TB ? ss : 0][j][t] = kTile * kRowBytes + kr * 512 + (((n >> 4) ^ kmaj_swz(kr)) << 5) + ((2 * n) & 31);
         }
       }
@@ -713,8 +773,10 @@ __device__ __forceinline__ void gemm_mainloop(const Operands& op, char* smem, f3
     // fragment reads complete before the barrier that releases this slot
     DMUON_WAIT_LGKM0();
   };
-  // diagonal fragment of 16-k chunk ss: this lane holds k = 16·ss + 8·h + e (e < 8)
-  // for row (A side) or column (B side) r32; its only nonzero element is k = r32.
+  // diagonal fragment of quarter R (A side: rows 16R .. of the 32-row block the
+  // stage's k cover; B side: columns): this lane holds k = 8(l >> 4) + e (e < 8)
+  // for row / column 16R + (l & 15); its only nonzero element is e = e0 + 16R
+  // with e0 = (l & 15) − 8(l >> 4).
   // e0 passes through an empty asm so that the fragments are built inside the
   // (rarely taken) diagonal branch instead of being hoisted out of the K loop,
   // where they would hold registers for the whole contraction.
@@ -729,34 +791,52 @@ __device__ __forceinline__ void gemm_mainloop(const Operands& op, char* smem, f3
   };
   auto mfma_phase = [&]() {
     __builtin_amdgcn_s_setprio(1);
+    if constexpr (kQ) {
+      // quarter (s, t): rows 16s of the wave's 128, columns 16t of its 64
+      static_for<8>([&](auto S) {
+        constexpr int qs = decltype(S)::value;
+        static_for<4>([&](auto Tq) {
+          constexpr int qt = decltype(Tq)::value;
+          mfma_quarter<2 * (qs & 1) + (qt & 1)>(acc[qs >> 1][qt >> 1], fa[qs >> 2][qs & 3], fb[qt >> 1][qt & 1]);
+        });
+      });
+    } else {
 #pragma unroll
-    for (int ss = 0; ss < 2; ++ss)
+      for (int ss = 0; ss < 2; ++ss)
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
+        for (int i = 0; i < 4; ++i)
 #pragma unroll
-        for (int j = 0; j < 2; ++j) mfma_chunk<T>(acc[i][j], fa[ss][i], fb[ss][j]);
+          for (int j = 0; j < 2; ++j) mfma_chunk<T>(acc[i][j], fa[ss][i], fb[ss][j]);
+    }
     __builtin_amdgcn_s_setprio(0);
   };
   // the extra MFMAs of a diagonal stage: block I of the wave's rows (A side) or
   // columns (B side)
   auto diag_phase = [&](auto I) {
     constexpr int b = decltype(I)::value;
-    int e0 = r32 - 8 * h;
+    int e0 = (lane & 15) - 8 * (lane >> 4);
     asm volatile("" : "+v"(e0));
     __builtin_amdgcn_s_setprio(1);
-#pragma unroll
-    for (int ss = 0; ss < 2; ++ss)
+    static_for<2>([&](auto Rq) {
+      constexpr int R = decltype(Rq)::value;
 #pragma unroll
       for (int p = 0; p < 2; ++p) {
-        const u32x4_t df = diag_frag(e0 - 16 * ss, p ? dg.a2 : dg.a1);
+        const u32x4_t df = diag_frag(e0 + 16 * R, p ? dg.a2 : dg.a1);
         if constexpr (DIAG == 1) {
-#pragma unroll
-          for (int j = 0; j < 2; ++j) mfma_chunk<T>(acc[b][j], df, fb[ss][j]);
+          // rows of quarter row R of block b against every column quarter
+          static_for<4>([&](auto Tq) {
+            constexpr int qt = decltype(Tq)::value;
+            mfma_quarter<2 * R + (qt & 1)>(acc[b][qt >> 1], df, fb[qt >> 1][qt & 1]);
+          });
         } else {
-#pragma unroll
-          for (int i = 0; i < 4; ++i) mfma_chunk<T>(acc[i][b], fa[ss][i], df);
+          // columns of quarter column R of block b against every row quarter
+          static_for<8>([&](auto S) {
+            constexpr int qs = decltype(S)::value;
+            mfma_quarter<2 * (qs & 1) + R>(acc[qs >> 1][b], fa[qs >> 2][qs & 3], df);
+          });
         }
       }
+    });
     __builtin_amdgcn_s_setprio(0);
   };
 
@@ -813,6 +893,12 @@ __device__ __forceinline__ void gemm_mainloop(const Operands& op, char* smem, f3
     for (int kt = kb + nb < KT ? kb + nb : KT; kt < KT; ++kt) step(kt);
   }
   if (lead) __builtin_amdgcn_s_barrier();              // every wave passes 2·KT + 2 barriers
+  if constexpr (kQ) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 2; ++j) quarters_to_32x32(acc[i][j]);
+  }
   // all LDS reads done before the caller reuses LDS
   __syncthreads();
 }
