@@ -26,8 +26,8 @@ the committed rocprofv3 kernel summaries are taken on).  ``--publish`` also writ
 bf16 published copy of every updated master inside the step.
 
 After the two passes the line's ``mfma_ceiling`` times the probe library's
-matrix-core-only waves (v_mfma_f32_32x32x16_bf16 on random register operands,
-the contraction kernels' instruction) for 3 s under the same board power
+matrix-core-only waves (v_mfma_f32_16x16x32_bf16 on random register operands,
+the bf16 contraction kernels' instruction) for 3 s under the same board power
 limit; ``roofline.frac_of_mfma_ceiling`` is the dominant kernel's rate over
 that ceiling.  ``--mfma-probe`` prints the ceiling of both instruction shapes on
 random and zero operands.
@@ -620,11 +620,12 @@ def main():
                        "target_frac": 0.8,
                        "note": "the decay + update runs inside the last apply launch (no separate kernel)"}
 
-    # the matrix cores alone on the dominant kernel's instruction, under the same
-    # power limit: the practical ceiling of a bf16 contraction on random operands
+    # the matrix cores alone on the dominant kernel's instruction (the bf16 path
+    # runs v_mfma_f32_16x16x32_bf16), under the same power limit: the practical
+    # ceiling of a bf16 contraction on random operands
     ceiling = None
     if roof and args.precision == "bf16" and not args.no_mfma_ceiling:
-        ceiling = mfma_ceiling(32, 0)
+        ceiling = mfma_ceiling(16, 0)
         roof["frac_of_mfma_ceiling"] = round(roof["achieved"] / ceiling["tflops"], 4)
 
     cpu = None

@@ -1,7 +1,7 @@
 /* dmuon_probe.h — a measurement probe that sits beside the Muon step library
  * (libdmuon_probe.so, built with it).  It is not part of the step.
  *
- * The step's contractions run on v_mfma_f32_32x32x16_bf16.  Under a sustained
+ * The step's bf16 contractions run on v_mfma_f32_16x16x32_bf16.  Under a sustained
  * load the board's power limit, not the 2.5 PFLOP/s dense bf16 figure, decides
  * how fast those instructions can go on operands with random bits.  The probe
  * measures that ceiling: every wave issues only matrix-core instructions on
