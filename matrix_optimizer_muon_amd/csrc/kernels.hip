@@ -484,7 +484,8 @@ __device__ __forceinline__ void buf_st(__amdgpu_buffer_rsrc_t r, unsigned off, u
 // Contraction core on the matrix cores: C[i][j] = Σ_k A(i, k)·B(j, k).
 //
 // One workgroup = 8 wave64s (two per SIMD) computing a 256×256 output tile; each
-// wave owns a 128×64 sub-tile (4×2 blocks of 32×32 MFMA output).  K is staged
+// wave owns a 128×64 sub-tile (4×2 blocks of 32×32 fp32 accumulators; on the bf16
+// path each block is computed as four 16×16×32 quarters, see mfma_quarter).  K is staged
 // through LDS in 64-byte rows (32 bf16 or 16 fp32 per row and stage), four stages
 // deep, filled by buffer_load … lds (global → LDS without VGPRs; rows beyond the
 // operand read as zero through the buffer's range check).  The four 16-byte
@@ -497,8 +498,8 @@ __device__ __forceinline__ void buf_st(__amdgpu_buffer_rsrc_t r, unsigned off, u
 // whole 512-byte row segments, so each DMA instruction moves 8 full cache lines
 // (the NT stage moves 16 half lines); its MFMA fragments are read with the
 // transposing ds_read_b64_tr_b16 (two 8-byte reads per 16-byte fragment).  Its
-// 32-byte segments are XOR-swizzled by 2·(row & 3), which spreads the 8 rows × 2
-// segments one fragment read touches over all 64 banks.  A K-major B operand
+// 32-byte segments are XOR-swizzled by kmaj_swz(row), which spreads the rows and
+// segments one half-wave of a fragment read touches over all 64 banks.  A K-major B operand
 // made plain 2048- to 8192-sized products 5–16% faster than NT; with both
 // operands K-major (twice the fragment reads) it is about even.  On the bf16
 // path X is kept only in storage layout, so the apply reads X (wide) or the
@@ -507,10 +508,10 @@ __device__ __forceinline__ void buf_st(__amdgpu_buffer_rsrc_t r, unsigned off, u
 //
 // Ping-pong schedule: the two waves sharing a SIMD belong to different groups
 // (group = wave >> 2, the 128-row half of the tile they own), and the groups run
-// one phase apart.  A phase is either an MFMA phase (16 MFMAs on the fragments
-// of one stage) or a memory phase (wait for the stage's DMA, read all of its
-// fragments, issue the DMA of the stage three ahead); a workgroup barrier ends
-// every phase.  While one group's waves keep the matrix cores busy, the other
+// one phase apart.  A phase is either an MFMA phase (the MFMAs on the fragments
+// of one stage: 32 of 16×16×32 on bf16, 64 of 32×32×2 on fp32) or a memory
+// phase (wait for the stage's DMA, read all of its fragments, issue the DMA of
+// the stage three ahead); a workgroup barrier ends every phase.  While one group's waves keep the matrix cores busy, the other
 // group's waves move data, so no barrier drains the MFMA pipeline.
 // ---------------------------------------------------------------------------
 constexpr int kGemmWaves = 8;
@@ -540,17 +541,6 @@ struct Operands {
 // of r spread a group's rows over four segment pairs and bit 3 moves the other
 // group's rows to the odd segments, so a half-wave touches 8 distinct segments.
 __device__ __forceinline__ int kmaj_swz(int r) { return (2 * (r & 3)) ^ ((r >> 3) & 1); }
-
-template <typename T>
-__device__ __forceinline__ void mfma_chunk(f32x16_t& acc, const u32x4_t& a, const u32x4_t& b);
-
-template <>
-__device__ __forceinline__ void mfma_chunk<uint16_t>(f32x16_t& acc, const u32x4_t& a, const u32x4_t& b) {
-  bf16x8_t va, vb;
-  __builtin_memcpy(&va, &a, 16);
-  __builtin_memcpy(&vb, &b, 16);
-  acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, vb, acc, 0, 0, 0);
-}
 
 // f(std::integral_constant<int, 0>{}) … f(std::integral_constant<int, N − 1>{})
 template <typename F, int... I>
@@ -601,11 +591,10 @@ __device__ __forceinline__ void quarters_to_32x32(f32x16_t& acc) {
     }
 }
 
-// fp32: a 16-byte chunk holds 4 consecutive k; element e of the two lane halves
-// forms one K = 2 step.  A and B use the same k permutation, so the sum covers
-// the same products.
-template <>
-__device__ __forceinline__ void mfma_chunk<float>(f32x16_t& acc, const u32x4_t& a, const u32x4_t& b) {
+// fp32 contraction step on one 32×32 block: a 16-byte chunk holds 4 consecutive
+// k; element e of the two lane halves forms one K = 2 step.  A and B use the same
+// k permutation, so the sum covers the same products.
+__device__ __forceinline__ void mfma_chunk_f32(f32x16_t& acc, const u32x4_t& a, const u32x4_t& b) {
   acc = __builtin_amdgcn_mfma_f32_32x32x2f32(__uint_as_float(a.x), __uint_as_float(b.x), acc, 0, 0, 0);
   acc = __builtin_amdgcn_mfma_f32_32x32x2f32(__uint_as_float(a.y), __uint_as_float(b.y), acc, 0, 0, 0);
   acc = __builtin_amdgcn_mfma_f32_32x32x2f32(__uint_as_float(a.z), __uint_as_float(b.z), acc, 0, 0, 0);
@@ -806,7 +795,7 @@ __device__ __forceinline__ void gemm_mainloop(const Operands& op, char* smem, f3
 #pragma unroll
         for (int i = 0; i < 4; ++i)
 #pragma unroll
-          for (int j = 0; j < 2; ++j) mfma_chunk<T>(acc[i][j], fa[ss][i], fb[ss][j]);
+          for (int j = 0; j < 2; ++j) mfma_chunk_f32(acc[i][j], fa[ss][i], fb[ss][j]);
     }
     __builtin_amdgcn_s_setprio(0);
   };
