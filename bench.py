@@ -114,7 +114,10 @@ def measured_mfma_busy(workload_name):
                                                         "mfma_busy": round(float(cells[4][:-1]) / 100, 4)}
     if sha != kernels_sha256() or not out:
         return None
-    return {"source": os.path.relpath(path, ROOT), "kernels": out}
+    return {"source": os.path.relpath(path, ROOT), "kernels": out,
+            "note": "mfma_busy is the share of the dispatch's cycles the matrix cores are busy; "
+                    "under the board's power limit a cheaper instruction raises the clock and "
+                    "lowers this share while the kernel gets faster"}
 
 
 def peak_clock_mhz(device_index):
