@@ -28,9 +28,15 @@ COMMON = ["-O3", "-std=c++17", "-fPIC", "-Wall", "-Wno-unused-function",
           "-I", os.path.join(os.path.dirname(HERE), "include")]
 
 
+# The probe's MFMAs keep their accumulators in VGPRs, as the step's contraction
+# kernels do (the compiler's choice there): with them in AGPRs a wave issues
+# 16×16×32 MFMAs at a lower rate and the probe would understate the ceiling.
+EXTRA = {"probe.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
+
+
 def _compile(src: str) -> str:
     obj = os.path.join(OBJ, src + ".o")
-    cmd = [HIPCC, *COMMON, "-c", os.path.join(CSRC, src), "-o", obj]
+    cmd = [HIPCC, *COMMON, *EXTRA.get(src, []), "-c", os.path.join(CSRC, src), "-o", obj]
     if src.endswith(".cpp"):
         cmd[1:1] = ["-x", "hip"]
     r = subprocess.run(cmd, capture_output=True, text=True)

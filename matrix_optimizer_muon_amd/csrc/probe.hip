@@ -2,6 +2,9 @@
 // MFMAs on register operands, so that a caller timing them for a few seconds
 // sees what the matrix cores sustain under the board's power limit with no
 // memory traffic.  Not part of the Muon step; the contract is in dmuon_probe.h.
+// The build compiles this file with the MFMA accumulators in VGPRs, where the
+// step's contraction kernels keep them: one wave per SIMD then issues 16×16×32
+// MFMAs at ~94% of the peak rate per clock, against ~71% with them in AGPRs.
 #include <hip/hip_runtime.h>
 
 #include <cstdint>
