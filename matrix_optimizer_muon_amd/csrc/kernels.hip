@@ -904,11 +904,14 @@ __device__ __forceinline__ int acc_col(int j) {
 
 // Tile orders.  Consecutive logical tiles run on one XCD in runs of 16 or 32 (see
 // xcd_logical_block), so the order decides how many operand panels one XCD's L2
-// has to hold at once.  Both orders walk bands of kBand tiles along one side of
-// the output and advance the other side every kBand tiles, so a run of 32 tiles
-// covers about 8 × 4 tiles and touches ~12 panels (a row-by-row order touched
-// ~33: for an 8192 × 28672 matrix, all 32 panels of B' per XCD and round).
+// has to hold at once.  Both orders walk bands of tiles along one side of the
+// output and advance the other side every band height, so a run of 32 tiles of
+// the apply or the square covers about 8 × 4 tiles and touches ~12 panels (a
+// row-by-row order touched ~33: for an 8192 × 28672 matrix, all 32 panels of B'
+// per XCD and round).  The Gram, in runs of 16, walks bands of 4: a run covers
+// about 4 × 4 tiles (8 panels, against 10 for 8 × 2).
 constexpr int kBand = 8;
+constexpr int kGramBand = 4;
 
 // apply: R tiles along the short side, C along the long one; returns the
 // short-side and long-side tile indices of logical tile u
@@ -922,12 +925,13 @@ __device__ __forceinline__ void band_tile(int u, int R, int C, int& ts, int& tl)
 }
 
 // Gram / square: upper-triangle tile u (ti ≤ tj) of a T×T grid.  Band b holds
-// rows [8b, 8b + h): first its triangle (tj from 8b to 8b + h − 1, each with
-// the rows up to tj), then h rows for every later tj.
+// rows [BAND·b, BAND·b + h): first its triangle (tj from BAND·b to BAND·b + h − 1,
+// each with the rows up to tj), then h rows for every later tj.
+template <int BAND>
 __device__ __forceinline__ void tri_tile(int u, int T, int& ti, int& tj) {
   int r0 = 0, start = 0;
   for (;;) {
-    const int h = T - r0 < kBand ? T - r0 : kBand;
+    const int h = T - r0 < BAND ? T - r0 : BAND;
     const int n = h * (h + 1) / 2 + h * (T - r0 - h);
     if (u < start + n) {
       int v = u - start;
@@ -945,7 +949,7 @@ __device__ __forceinline__ void tri_tile(int u, int T, int& ti, int& tj) {
       return;
     }
     start += n;
-    r0 += kBand;
+    r0 += BAND;
   }
 }
 
@@ -1563,7 +1567,7 @@ __global__ __launch_bounds__(kGemmThreads) void k_gemm(LaunchTable tab, LaunchSc
     const int per = T_ * (T_ + 1) / 2;
     slice = local / per;
     u = local % per;
-    tri_tile(u, T_, ti, tj);
+    tri_tile<PH == PH_GRAM ? kGramBand : kBand>(u, T_, ti, tj);
     row0 = ti * kTile;
     col0 = tj * kTile;
     const int ld = PH == PH_GRAM ? P.ld_n : P.ld_m;
