@@ -902,14 +902,14 @@ __device__ __forceinline__ int acc_col(int j) {
   return (wave & 3) * 64 + j * 32 + (lane & 31);
 }
 
-// Tile orders.  Consecutive logical tiles run on one XCD in runs of 16 or 32 (see
+// Tile orders.  Consecutive logical tiles run on one XCD in runs of 16 or 64 (see
 // xcd_logical_block), so the order decides how many operand panels one XCD's L2
 // has to hold at once.  Both orders walk bands of tiles along one side of the
-// output and advance the other side every band height, so a run of 32 tiles of
-// the apply covers about 8 × 4 tiles and touches ~12 panels (a row-by-row order
-// touched ~33: for an 8192 × 28672 matrix, all 32 panels of B' per XCD and
-// round).  The Gram and the square, in runs of 16, walk bands of 4: a run covers
-// about 4 × 4 tiles (8 panels, against 10 for 8 × 2).
+// output and advance the other side every band height, so the 32 apply tiles
+// one XCD runs at once cover about 8 × 4 tiles and touch ~12 panels (a
+// row-by-row order touched ~33: for an 8192 × 28672 matrix, all 32 panels of B'
+// per XCD and round).  The Gram and the square, in runs of 16, walk bands of 4:
+// a run covers about 4 × 4 tiles (8 panels, against 10 for 8 × 2).
 constexpr int kBand = 8;
 constexpr int kTriBand = 4;
 
@@ -961,8 +961,8 @@ __device__ __forceinline__ void tri_tile(int u, int T, int& ti, int& tj) {
 // unequal cost (long-K problems first) are spread over every XCD.  A last
 // partial window of R tiles is split the same way into 8 contiguous runs (the
 // first R % 8 XCDs take one tile more).  The map is a bijection on [0, G).
-// Runs of 32 suit the apply; the Gram and the square (triangle tiles in bands of
-// 4) measured faster with runs of 16.
+// Runs of 64 suit the apply (two rounds of 8 × 4 tiles per XCD); the Gram and
+// the square (triangle tiles in bands of 4) measured faster with runs of 16.
 template <int RUN>
 __device__ __forceinline__ int xcd_logical_block() {
   const int G = gridDim.x, b = blockIdx.x;
@@ -1552,7 +1552,7 @@ __global__ __launch_bounds__(kGemmThreads) void k_gemm(LaunchTable tab, LaunchSc
   __shared__ float red[kGemmWaves];
   constexpr int kElemsPerRow = kRowBytes / (int)sizeof(T);
   constexpr bool kKmaj = sizeof(T) == 2;     // bf16: one storage-layout copy of X, K-major reads
-  const int bid = xcd_logical_block<PH == PH_APPLY ? 32 : 16>();
+  const int bid = xcd_logical_block<PH == PH_APPLY ? 64 : 16>();
   const int p = find_prob(tab.wg_prefix + PH * (tab.n_probs + 1), tab.n_probs, bid);
   const DevProblem& P = tab.probs[p];
   if (P.tag != tab.tag) return;      // the workspace holds another plan's table
